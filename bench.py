@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""WKV7 forward + backward throughput on one MI355X.
+
+One step = the whole hot path over one batch of synthetic inputs already
+resident in HBM: the forward scan (writing y, the final state and the
+checkpoints every `chunk` steps) followed by the reverse scan that consumes
+those checkpoints and writes dr, dw, dk, dv, da, db and ds0.
+
+Prints ONE JSON line.  `value` is tokens (B*T) per second of fwd+bwd.
+`roofline` is for the dominant kernel (the reverse scan): its algorithmic
+fp32 flops per launch (26*N^2 per token-head) over its mean launch time,
+timed with HIP events on the stream it runs on, against the MI355X fp32
+vector peak.  `cpu_baseline` times the fp64 oracle on a bounded sample of
+whole (b, h) recurrences of the same workload on the host's cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "WKV7 fwd+bwd tokens/sec at 1 GPU; % of HBM/VALU roofline (rocprof)"
+PEAK_FP32_VALU = 157.3e12   # MI355X published fp32 vector peak (FLOP/s)
+PEAK_HBM = 8.0e12           # MI355X HBM3E (B/s)
+DEFAULT_WORKLOAD = "b8_t4096_h32_n64"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ("linear_attention_rnn_wkv7_amd/csrc/wkv7_bwd.hip",
+                  "linear_attention_rnn_wkv7_amd/csrc/wkv7_device.h")
+
+
+def algorithmic(wl):
+    """Algorithmic work per launch (fp32 flops with FMA = 2, HBM bytes)."""
+    th = wl.B * wl.T * wl.H
+    N = wl.N
+    eb = 4 if wl.dtype == "f32" else 2
+    ck = 4 * N * N / wl.chunk                     # checkpoint bytes per token-head
+    fwd_flops = 9 * N * N * th
+    bwd_flops = 26 * N * N * th
+    fwd_bytes = (6 * N * eb + 4 * N + ck) * th    # r,w,k,v,a,b in; y out; ckpt out
+    bwd_bytes = (7 * N * eb + 6 * N * 4 + ck) * th  # 7 vectors in; 6 grads out; ckpt in
+    return fwd_flops, bwd_flops, fwd_bytes, bwd_bytes
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per backward launch from committed rocprofv3 counter runs,
+    or None when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"wkv7_bwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, wl, budget_s):
+    """Time the fp64 oracle (fwd + bwd) on whole (b, h) recurrences."""
+    import numpy as np
+
+    import oracle
+    from linear_attention_rnn_wkv7_amd.synthetic import state_slice, vec_slice
+
+    cores = oracle.default_threads()
+    names = ("r", "w", "k", "v", "a", "b", "dy")
+
+    def sample(pairs):
+        def c64(x):
+            return x.detach().to("cpu").double().numpy()
+        sl = {n: np.concatenate([c64(vec_slice(inp[n], b, h)) for b, h in pairs], 2)
+              for n in names}
+        s0 = None if inp["s0"] is None else np.concatenate(
+            [c64(state_slice(inp["s0"], b, h)) for b, h in pairs], 1)
+        dsT = None if inp["dsT"] is None else np.concatenate(
+            [c64(state_slice(inp["dsT"], b, h)) for b, h in pairs], 1)
+        return sl, s0, dsT
+
+    def run(pairs):
+        sl, s0, dsT = sample(pairs)
+        threads = min(cores, len(pairs))
+        t = time.perf_counter()
+        oracle.forward(*(sl[n] for n in names[:6]), s0=s0, want_sT=True, threads=threads)
+        oracle.backward(*(sl[n] for n in names[:6]), sl["dy"], s0=s0, dsT=dsT,
+                        threads=threads)
+        return time.perf_counter() - t, threads
+
+    all_pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)]
+    probe_t, _ = run(all_pairs[:1])
+    # one pair per core per round; as many pairs as fit the time budget
+    n = int(max(1, min(len(all_pairs), cores * max(1, int(budget_s / max(probe_t, 1e-3))))))
+    n = min(n, cores * 4)
+    pairs = all_pairs[:n]
+    dt, threads = run(pairs)
+    token_heads = len(pairs) * wl.T
+    return {
+        "value": token_heads / dt / wl.H,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(pairs)} of {wl.B * wl.H} whole (b,h) recurrences (T={wl.T}), "
+                  f"fp64 fwd+bwd in {dt:.1f} s; tokens/s = token-heads/s / H",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} (world {world}) is not "
+              "supported; each (b, h) recurrence is independent, so N GPUs would each run "
+              "1/N of the heads with no communication.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from linear_attention_rnn_wkv7_amd import api
+    from linear_attention_rnn_wkv7_amd.synthetic import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    names = ("r", "w", "k", "v", "a", "b")
+    inp = make_inputs(wl, device="cuda")
+    B, T, H, N, C = wl.B, wl.T, wl.H, wl.N, wl.chunk
+    dev = inp["r"].device
+    f32 = torch.float32
+    y = torch.empty((B, T, H, N), device=dev, dtype=f32)
+    sT = torch.empty((B, H, N, N), device=dev, dtype=f32)
+    ck = torch.empty((B, H, (T + C - 1) // C, N, N), device=dev, dtype=f32)
+    grads = {n: torch.empty((B, T, H, N), device=dev, dtype=f32)
+             for n in ("dr", "dw", "dk", "dv", "da", "db")}
+    grads["ds0"] = torch.empty((B, H, N, N), device=dev, dtype=f32)
+    need = api.wkv7_backward_workspace_bytes(B, T, H, N, inp["r"].dtype, C, True)
+    ws = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        api.wkv7_forward(*(inp[n] for n in names), inp["s0"], chunk=C, want_ckpt=True,
+                         out=(y, sT, ck), stream=stream)
+        if ev:
+            ev[1].record(stream)
+        api.wkv7_backward(*(inp[n] for n in names), inp["dy"], inp["s0"], inp["dsT"], ck,
+                          chunk=C, workspace=ws, out=grads, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    for n, x in list(grads.items()) + [("y", y), ("sT", sT)]:
+        if not torch.isfinite(x).all():
+            raise RuntimeError(f"non-finite values in {n}")
+
+    fwd_flops, bwd_flops, fwd_bytes, bwd_bytes = algorithmic(wl)
+    achieved = bwd_flops / (bwd_ms * 1e-3)
+    traffic = measured_traffic(wl.name)
+    t_roof = max((fwd_flops + bwd_flops) / PEAK_FP32_VALU, (fwd_bytes + bwd_bytes) / PEAK_HBM)
+    tokens = B * T
+    rec = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "N": N, "chunk": C,
+                   "input_dtype": wl.dtype, "s0": wl.has_s0, "dsT": wl.has_dsT},
+        "roofline": {
+            "kernel": "wkv7_bwd_kernel",
+            "bound": "alu",
+            "achieved": achieved / 1e12,
+            "peak": PEAK_FP32_VALU / 1e12,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_VALU,
+            "traffic": traffic,
+        },
+        "fwd_ms": fwd_ms,
+        "bwd_ms": bwd_ms,
+        "fwd_bwd_roofline_frac": t_roof / (ms * 1e-3),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

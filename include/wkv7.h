@@ -1,0 +1,134 @@
+/*
+ * wkv7.h -- C ABI of libwkv7: the WKV7 (RWKV-7) matrix-state recurrence and
+ * its reverse (backward-through-time) scan on MI355X (gfx950).
+ *
+ * The operation (Foundry page "rwkvx/rx_pretrain.c": rx_wkv7_forward_seq for
+ * the forward, rx_wkv7_backward and the comment block above it for the
+ * reverse scan; the flat index helpers vx/sx there fix the layouts).  For
+ * every batch b and head h independently, with S[i][j] (i = value row,
+ * j = key column) starting at s0:
+ *
+ *     sa_t = S_{t-1} a_t
+ *     S_t  = S_{t-1} diag(w_t) + v_t k_t^T + sa_t b_t^T
+ *     y_t  = S_t r_t
+ *
+ * The backward returns the exact gradient of
+ *     L = sum_t <dy_t, y_t> + <dsT, S_{T-1}>
+ * with respect to r, w, k, v, a, b and s0.  (The page seeds the reverse scan
+ * with a zero state gradient; the dsT input is the extension the burn_mamba
+ * serial_recalculated backward.rs page makes with its d_final_state input.)
+ * w is the multiplicative decay itself and dw is dL/dw for that multiplier.
+ *
+ * Layouts (all row-major, contiguous):
+ *   vectors r, w, k, v, a, b, dy, y, dr, dw, dk, dv, da, db : [B][T][H][N]
+ *   states  s0, sT, dsT, ds0                                 : [B][H][N][N] fp32
+ *   checkpoints ckpt : [B][H][ceil(T/C)][N][N] fp32; slot c holds the state
+ *                      before step c*C (slot 0 = s0, or zeros).
+ * Inputs r..b and dy are fp32 or bf16 (wkv7_shape.dtype); everything else,
+ * including y and all gradients, is fp32.
+ *
+ * Ownership and execution: every pointer is caller-owned DEVICE memory,
+ * 16-byte aligned.  Calls only enqueue work on `stream` (NULL = the default
+ * stream) and return; the library never allocates, frees or synchronises.
+ * Results are deterministic (fixed reduction order, no float atomics).
+ * There is no global mutable state: concurrent calls on different streams
+ * are safe when their output buffers do not overlap.
+ *
+ * Errors: every argument is validated before anything is enqueued; a
+ * negative status means nothing was written.  WKV7_ERR_HIP reports a launch
+ * failure (from hipGetLastError) after validation passed.
+ */
+#ifndef WKV7_H
+#define WKV7_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype of the inputs r, w, k, v, a, b and dy. */
+typedef enum {
+    WKV7_F32 = 0,
+    WKV7_BF16 = 1
+} wkv7_dtype;
+
+typedef struct {
+    int64_t B;      /* batch, >= 0 */
+    int64_t T;      /* time steps, >= 0 */
+    int64_t H;      /* heads, >= 0 */
+    int64_t N;      /* head size; 16 and 64 are supported */
+    int32_t dtype;  /* wkv7_dtype */
+    int32_t chunk;  /* checkpoint interval C: 0 means 64; else a multiple of
+                       8 in [8, 4096] */
+} wkv7_shape;
+
+enum {
+    WKV7_OK = 0,
+    WKV7_ERR_INVALID = -1,      /* NULL/misaligned pointer, negative size,
+                                   bad dtype or chunk, size overflow */
+    WKV7_ERR_UNSUPPORTED = -2,  /* N not in {16, 64} */
+    WKV7_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+    WKV7_ERR_HIP = -4           /* a kernel launch failed */
+};
+
+/* Bytes of the checkpoint buffer for `shape` (B*H*ceil(T/C)*N*N*4); 0 when
+ * the shape is invalid or empty. */
+size_t wkv7_checkpoint_bytes(const wkv7_shape *shape);
+
+/* Bytes of device workspace wkv7_backward needs: the per-(b,h) state
+ * sub-checkpoints of one chunk, plus room for the checkpoints themselves
+ * when `ckpt_provided` is 0.  0 when the shape is invalid or empty. */
+size_t wkv7_backward_workspace_bytes(const wkv7_shape *shape, int ckpt_provided);
+
+/* Forward scan (rx_wkv7_forward_seq on the Foundry rx_pretrain.c page).
+ *   r, w, k, v, a, b : inputs, [B][T][H][N], dtype per shape->dtype; required
+ *                      unless B*T*H == 0.
+ *   s0   : initial state, fp32 [B][H][N][N]; NULL means zeros.
+ *   y    : output, fp32 [B][T][H][N]; NULL skips it.
+ *   sT   : final state, fp32 [B][H][N][N]; NULL skips it.
+ *   ckpt : checkpoints for wkv7_backward, wkv7_checkpoint_bytes(shape) bytes;
+ *          NULL skips them.
+ * With T == 0, sT receives s0 (or zeros). */
+int wkv7_forward(const wkv7_shape *shape,
+                 const void *r, const void *w, const void *k, const void *v,
+                 const void *a, const void *b, const float *s0,
+                 float *y, float *sT, float *ckpt, hipStream_t stream);
+
+/* Reverse scan (rx_wkv7_backward on the Foundry rx_pretrain.c page, seeded
+ * with dsT).
+ *   r..b, dy : inputs as for the forward; dy is dL/dy, [B][T][H][N].
+ *   s0   : the forward's initial state (NULL = zeros); read only when
+ *          ckpt is NULL.
+ *   dsT  : dL/d(final state), fp32 [B][H][N][N]; NULL means zeros.
+ *   ckpt : the checkpoints a wkv7_forward call with the same inputs, s0 and
+ *          chunk wrote; NULL makes the backward recompute them into the
+ *          workspace first.
+ *   dr, dw, dk, dv, da, db : outputs, fp32 [B][T][H][N], all required.
+ *   ds0  : dL/ds0, fp32 [B][H][N][N]; NULL skips it.
+ *   workspace, workspace_bytes : device scratch of at least
+ *          wkv7_backward_workspace_bytes(shape, ckpt != NULL) bytes; its
+ *          contents on entry do not matter.
+ * With T == 0, ds0 receives dsT (or zeros). */
+int wkv7_backward(const wkv7_shape *shape,
+                  const void *r, const void *w, const void *k, const void *v,
+                  const void *a, const void *b, const float *s0,
+                  const void *dy, const float *dsT, const float *ckpt,
+                  float *dr, float *dw, float *dk, float *dv, float *da, float *db,
+                  float *ds0, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/* Static text for a status code. */
+const char *wkv7_status_string(int status);
+
+/* ABI version (major * 100 + minor). */
+int wkv7_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV7_H */

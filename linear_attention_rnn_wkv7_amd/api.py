@@ -1,0 +1,112 @@
+"""Thin torch-facing binding of the libwkv7 C ABI.
+
+Argument marshalling only: torch allocates device memory and supplies the
+stream; every step of the recurrence runs in the library's HIP kernels.
+Names mirror the C entry points (include/wkv7.h).
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+
+_VEC_DTYPES = {torch.float32: _lib.WKV7_F32, torch.bfloat16: _lib.WKV7_BF16}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_shape(B, T, H, N, dtype=torch.float32, chunk=64):
+    return _lib.Shape(B, T, H, N, _VEC_DTYPES[dtype], chunk)
+
+
+def _check_vecs(names, tensors):
+    ref = tensors[0]
+    if ref.dim() != 4:
+        raise ValueError(f"{names[0]} must be [B, T, H, N]")
+    if ref.dtype not in _VEC_DTYPES:
+        raise ValueError(f"{names[0]}: dtype {ref.dtype} not supported")
+    for n, t in zip(names, tensors):
+        if t.shape != ref.shape or t.dtype != ref.dtype:
+            raise ValueError(f"{n}: shape/dtype must match {names[0]}")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous device tensor")
+    return tuple(ref.shape), ref.dtype
+
+
+def _check_state(name, t, B, H, N):
+    if t is None:
+        return
+    if t.shape != (B, H, N, N) or t.dtype != torch.float32 or not t.is_cuda \
+            or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous fp32 device tensor [B, H, N, N]")
+
+
+def wkv7_checkpoint_bytes(B, T, H, N, dtype=torch.float32, chunk=64):
+    sh = make_shape(B, T, H, N, dtype, chunk)
+    return _lib.lib().wkv7_checkpoint_bytes(ctypes.byref(sh))
+
+
+def wkv7_backward_workspace_bytes(B, T, H, N, dtype=torch.float32, chunk=64, ckpt_provided=True):
+    sh = make_shape(B, T, H, N, dtype, chunk)
+    return _lib.lib().wkv7_backward_workspace_bytes(ctypes.byref(sh), int(bool(ckpt_provided)))
+
+
+def wkv7_forward(r, w, k, v, a, b, s0=None, *, chunk=64, want_y=True, want_sT=True,
+                 want_ckpt=False, stream=None, out=None):
+    """Run the forward scan.  Returns (y, sT, ckpt); unwanted outputs are None.
+
+    ``out`` may supply preallocated (y, sT, ckpt) tensors (None entries are
+    allocated when wanted)."""
+    (B, T, H, N), dt = _check_vecs("rwkvab", (r, w, k, v, a, b))
+    _check_state("s0", s0, B, H, N)
+    dev = r.device
+    y, sT, ckpt = out if out is not None else (None, None, None)
+    if want_y and y is None:
+        y = torch.empty((B, T, H, N), device=dev, dtype=torch.float32)
+    if want_sT and sT is None:
+        sT = torch.empty((B, H, N, N), device=dev, dtype=torch.float32)
+    if want_ckpt and ckpt is None:
+        nck = (T + chunk - 1) // chunk
+        ckpt = torch.empty((B, H, nck, N, N), device=dev, dtype=torch.float32)
+    sh = make_shape(B, T, H, N, dt, chunk)
+    rc = _lib.lib().wkv7_forward(ctypes.byref(sh), *map(_ptr, (r, w, k, v, a, b, s0)),
+                                 _ptr(y if want_y else None), _ptr(sT if want_sT else None),
+                                 _ptr(ckpt if want_ckpt else None), _stream(stream))
+    _lib.check("wkv7_forward", rc)
+    return (y if want_y else None), (sT if want_sT else None), (ckpt if want_ckpt else None)
+
+
+def wkv7_backward(r, w, k, v, a, b, dy, s0=None, dsT=None, ckpt=None, *, chunk=64,
+                  want_ds0=True, workspace=None, stream=None, out=None):
+    """Run the reverse scan.  Returns dict(dr, dw, dk, dv, da, db, ds0)."""
+    (B, T, H, N), dt = _check_vecs("rwkvab dy", (r, w, k, v, a, b, dy))
+    _check_state("s0", s0, B, H, N)
+    _check_state("dsT", dsT, B, H, N)
+    dev = r.device
+    names = ("dr", "dw", "dk", "dv", "da", "db")
+    grads = dict(out) if out is not None else {}
+    for n in names:
+        if grads.get(n) is None:
+            grads[n] = torch.empty((B, T, H, N), device=dev, dtype=torch.float32)
+    if want_ds0 and grads.get("ds0") is None:
+        grads["ds0"] = torch.empty((B, H, N, N), device=dev, dtype=torch.float32)
+    if not want_ds0:
+        grads["ds0"] = None
+    need = wkv7_backward_workspace_bytes(B, T, H, N, dt, chunk, ckpt is not None)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sh = make_shape(B, T, H, N, dt, chunk)
+    rc = _lib.lib().wkv7_backward(
+        ctypes.byref(sh), *map(_ptr, (r, w, k, v, a, b, s0, dy, dsT, ckpt)),
+        *map(_ptr, (grads[n] for n in names)), _ptr(grads["ds0"]),
+        _ptr(workspace), ws_bytes, _stream(stream))
+    _lib.check("wkv7_backward", rc)
+    return grads

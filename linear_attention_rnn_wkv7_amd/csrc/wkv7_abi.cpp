@@ -1,0 +1,222 @@
+// libwkv7 C ABI: argument validation, workspace layout and dispatch.
+// Every check runs before anything is enqueued on the stream.
+
+#include "wkv7.h"
+
+#include <stdint.h>
+
+#include "wkv7_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;   // workspace sub-buffer alignment
+
+struct Dims {
+    int64_t B, T, H, N, C, nck;
+    int dtype;
+    size_t vec_elems, state_elems;   // per tensor
+};
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out)
+{
+    return !__builtin_mul_overflow(a, b, out);
+}
+
+int check_shape(const wkv7_shape *s, Dims *d)
+{
+    if (!s) return WKV7_ERR_INVALID;
+    if (s->B < 0 || s->T < 0 || s->H < 0 || s->N <= 0) return WKV7_ERR_INVALID;
+    if (s->dtype != WKV7_F32 && s->dtype != WKV7_BF16) return WKV7_ERR_INVALID;
+    const int64_t C = s->chunk == 0 ? 64 : s->chunk;
+    if (C < 8 || C > 4096 || C % 8 != 0) return WKV7_ERR_INVALID;
+    if (s->N != 16 && s->N != 64) return WKV7_ERR_UNSUPPORTED;
+    int64_t bh, bth, vec, st, nck_elems, bytes;
+    if (!mul_ok(s->B, s->H, &bh) || bh > INT32_MAX) return WKV7_ERR_INVALID;
+    if (!mul_ok(bh, s->T, &bth) || !mul_ok(bth, s->N, &vec)) return WKV7_ERR_INVALID;
+    if (!mul_ok(vec, 4, &bytes)) return WKV7_ERR_INVALID;
+    if (!mul_ok(bh, s->N * s->N, &st)) return WKV7_ERR_INVALID;
+    const int64_t nck = (s->T + C - 1) / C;
+    if (nck > INT32_MAX) return WKV7_ERR_INVALID;
+    if (!mul_ok(st, nck, &nck_elems) || !mul_ok(nck_elems, 4, &bytes)) return WKV7_ERR_INVALID;
+    d->B = s->B;
+    d->T = s->T;
+    d->H = s->H;
+    d->N = s->N;
+    d->C = C;
+    d->nck = nck;
+    d->dtype = s->dtype;
+    d->vec_elems = (size_t)vec;
+    d->state_elems = (size_t)st;
+    return WKV7_OK;
+}
+
+bool aligned(const void *p)
+{
+    return ((uintptr_t)p & 15u) == 0;
+}
+
+size_t round_up(size_t x)
+{
+    return (x + kAlign - 1) / kAlign * kAlign;
+}
+
+size_t ckpt_bytes(const Dims &d)
+{
+    return d.state_elems * (size_t)d.nck * sizeof(float);
+}
+
+// Sub-checkpoint scratch first, then (when needed) the checkpoints.
+size_t workspace_bytes(const Dims &d, bool ckpt_provided)
+{
+    size_t n = round_up(wkv7::sub_bytes(d.B, d.H, d.N, (int)d.C));
+    if (!ckpt_provided) n += round_up(ckpt_bytes(d));
+    return n;
+}
+
+int hip_status(hipError_t e)
+{
+    return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wkv7_checkpoint_bytes(const wkv7_shape *shape)
+{
+    Dims d;
+    if (check_shape(shape, &d) != WKV7_OK) return 0;
+    return ckpt_bytes(d);
+}
+
+size_t wkv7_backward_workspace_bytes(const wkv7_shape *shape, int ckpt_provided)
+{
+    Dims d;
+    if (check_shape(shape, &d) != WKV7_OK || d.B * d.H == 0 || d.T == 0) return 0;
+    return workspace_bytes(d, ckpt_provided != 0);
+}
+
+int wkv7_forward(const wkv7_shape *shape, const void *r, const void *w, const void *k,
+                 const void *v, const void *a, const void *b, const float *s0,
+                 float *y, float *sT, float *ckpt, hipStream_t stream)
+{
+    Dims d;
+    int rc = check_shape(shape, &d);
+    if (rc != WKV7_OK) return rc;
+    if (d.B * d.H == 0) return WKV7_OK;
+    const void *in[6] = {r, w, k, v, a, b};
+    for (const void *p : in) {
+        if (d.T > 0 && !p) return WKV7_ERR_INVALID;
+        if (!aligned(p)) return WKV7_ERR_INVALID;
+    }
+    for (const void *p : {(const void *)s0, (const void *)y, (const void *)sT, (const void *)ckpt})
+        if (!aligned(p)) return WKV7_ERR_INVALID;
+
+    if (d.T == 0) {
+        if (!sT) return WKV7_OK;
+        return hip_status(wkv7::launch_fill(sT, s0, d.state_elems, stream));
+    }
+    wkv7::FwdLaunch L;
+    for (int i = 0; i < 6; ++i) L.in[i] = in[i];
+    L.s0 = s0;
+    L.y = y;
+    L.sT = sT;
+    L.ckpt = ckpt;
+    L.B = d.B;
+    L.T = d.T;
+    L.H = d.H;
+    L.N = d.N;
+    L.dtype = d.dtype;
+    L.chunk = (int)d.C;
+    return hip_status(wkv7::launch_forward(L, stream));
+}
+
+int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const void *k,
+                  const void *v, const void *a, const void *b, const float *s0,
+                  const void *dy, const float *dsT, const float *ckpt,
+                  float *dr, float *dw, float *dk, float *dv, float *da, float *db,
+                  float *ds0, void *workspace, size_t workspace_bytes_given,
+                  hipStream_t stream)
+{
+    Dims d;
+    int rc = check_shape(shape, &d);
+    if (rc != WKV7_OK) return rc;
+    if (d.B * d.H == 0) return WKV7_OK;
+    const void *in[7] = {r, w, k, v, a, b, dy};
+    float *grad[6] = {dr, dw, dk, dv, da, db};
+    for (const void *p : in) {
+        if (d.T > 0 && !p) return WKV7_ERR_INVALID;
+        if (!aligned(p)) return WKV7_ERR_INVALID;
+    }
+    for (float *p : grad) {
+        if (d.T > 0 && !p) return WKV7_ERR_INVALID;
+        if (!aligned(p)) return WKV7_ERR_INVALID;
+    }
+    for (const void *p : {(const void *)s0, (const void *)dsT, (const void *)ckpt,
+                          (const void *)ds0})
+        if (!aligned(p)) return WKV7_ERR_INVALID;
+
+    if (d.T == 0) {
+        if (!ds0) return WKV7_OK;
+        return hip_status(wkv7::launch_fill(ds0, dsT, d.state_elems, stream));
+    }
+    const size_t need = workspace_bytes(d, ckpt != nullptr);
+    if (need > 0 && (!workspace || workspace_bytes_given < need)) return WKV7_ERR_WORKSPACE;
+    if (((uintptr_t)workspace % kAlign) != 0) return WKV7_ERR_WORKSPACE;
+
+    char *ws = static_cast<char *>(workspace);
+    float *sub = reinterpret_cast<float *>(ws);
+    const float *ck = ckpt;
+    if (!ckpt) {
+        float *own = reinterpret_cast<float *>(
+            ws + round_up(wkv7::sub_bytes(d.B, d.H, d.N, (int)d.C)));
+        wkv7::FwdLaunch F;
+        for (int i = 0; i < 6; ++i) F.in[i] = in[i];
+        F.s0 = s0;
+        F.y = nullptr;
+        F.sT = nullptr;
+        F.ckpt = own;
+        F.B = d.B;
+        F.T = d.T;
+        F.H = d.H;
+        F.N = d.N;
+        F.dtype = d.dtype;
+        F.chunk = (int)d.C;
+        rc = hip_status(wkv7::launch_forward(F, stream));
+        if (rc != WKV7_OK) return rc;
+        ck = own;
+    }
+    wkv7::BwdLaunch L;
+    for (int i = 0; i < 7; ++i) L.in[i] = in[i];
+    L.ckpt = ck;
+    L.dsT = dsT;
+    for (int i = 0; i < 6; ++i) L.grad[i] = grad[i];
+    L.ds0 = ds0;
+    L.sub = sub;
+    L.B = d.B;
+    L.T = d.T;
+    L.H = d.H;
+    L.N = d.N;
+    L.dtype = d.dtype;
+    L.chunk = (int)d.C;
+    return hip_status(wkv7::launch_backward(L, stream));
+}
+
+const char *wkv7_status_string(int status)
+{
+    switch (status) {
+    case WKV7_OK: return "ok";
+    case WKV7_ERR_INVALID: return "invalid argument";
+    case WKV7_ERR_UNSUPPORTED: return "unsupported head size";
+    case WKV7_ERR_WORKSPACE: return "workspace missing or too small";
+    case WKV7_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+    }
+}
+
+int wkv7_abi_version(void)
+{
+    return 100;
+}
+
+}  // extern "C"

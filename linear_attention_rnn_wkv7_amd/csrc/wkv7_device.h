@@ -1,0 +1,133 @@
+// Device-side helpers shared by the WKV7 kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkv7 {
+
+constexpr int kWave = 64;
+
+// DPP controls (GFX9 DPP16 encodings).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane l <- 7-l within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane l <- 15-l within each 16 lanes
+constexpr int kDppRor4 = 0x124;       // lane l <- (l+4) mod 16 within the row
+constexpr int kDppRor8 = 0x128;       // lane l <- (l+8) mod 16 within the row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the LPR consecutive lanes (LPR in {4, 8, 16}, aligned groups);
+// every lane of the group receives the sum.
+template <int LPR>
+__device__ __forceinline__ float group_allreduce(float x)
+{
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16, "group size");
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    if constexpr (LPR >= 8) x += dpp<kDppHalfMirror>(x);
+    if constexpr (LPR >= 16) x += dpp<kDppMirror>(x);
+    return x;
+}
+
+// Exchange-and-add across lane bit 5: the result in lanes 0-31 is x summed
+// over lane l and l^32; in lanes 32-63 it is y summed the same way.
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second.  Written as inline asm: this compiler folds the
+// sum of the two results of __builtin_amdgcn_permlane32_swap into twice the
+// first result.  The s_nop 1 pairs keep two wait states around the swap.
+__device__ __forceinline__ float swap_add32(float x, float y)
+{
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+    return x + y;
+}
+
+// The same across lane bit 4 (v_permlane16_swap exchanges the odd 16-lane
+// rows of its first operand with the even rows of its second): lanes with
+// bit 4 clear get x summed over l and l^16, lanes with bit 4 set get y.
+__device__ __forceinline__ float swap_add16(float x, float y)
+{
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+    return x + y;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
+
+// 4 consecutive input elements, loaded raw (fp32: 16 bytes, bf16: 8 bytes)
+// and widened to fp32.
+template <typename TIn>
+struct InQuad {
+    using raw = float4;
+    __device__ static raw load(const TIn *p) { return *reinterpret_cast<const float4 *>(p); }
+    __device__ static float4 f32(raw q) { return q; }
+};
+
+template <>
+struct InQuad<uint16_t> {   // bf16 stored as raw 16-bit patterns
+    using raw = uint2;
+    __device__ static raw load(const uint16_t *p) { return *reinterpret_cast<const uint2 *>(p); }
+    __device__ static float4 f32(raw q)
+    {
+        return make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));
+    }
+};
+
+// Base pointers of NV input vectors with the same [B][T][H][N] layout.
+template <typename TIn, int NV>
+struct VecPtrs {
+    const TIn *p[NV];
+    // Pointer of vector q (q may differ per lane): a select chain over kernel
+    // arguments, so no pointer array is indexed dynamically.
+    __device__ __forceinline__ const TIn *get(int q) const
+    {
+        const TIn *src = p[0];
+#pragma unroll
+        for (int i = 1; i < NV; ++i)
+            if (q == i) src = p[i];
+        return src;
+    }
+};
+
+// Copies the per-step vectors of one (b, h) for steps [t0, t0 + nsteps) into
+// registers (issue) and then into LDS (commit) as fp32, laid out
+// lds[vec][step][n].  Steps past nsteps are not loaded.
+template <typename TIn, int NV, int TB, int N, int NTHREADS>
+struct Stager {
+    static constexpr int kUnits = NV * TB * N / 4;
+    static constexpr int kPer = (kUnits + NTHREADS - 1) / NTHREADS;
+    typename InQuad<TIn>::raw buf[kPer];
+
+    __device__ __forceinline__ void issue(const VecPtrs<TIn, NV> &vec, int64_t base_t0,
+                                          int64_t step_stride, int nsteps, int tid)
+    {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int unit = tid + u * NTHREADS;
+            const int n4 = unit % (N / 4);
+            const int st = (unit / (N / 4)) % TB;
+            const int q = unit / (TB * N / 4);
+            if (unit < kUnits && st < nsteps)
+                buf[u] = InQuad<TIn>::load(vec.get(q) + base_t0 + st * step_stride + 4 * n4);
+        }
+    }
+
+    __device__ __forceinline__ void commit(float *lds, int nsteps, int tid)
+    {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int unit = tid + u * NTHREADS;
+            const int st = (unit / (N / 4)) % TB;
+            if (unit < kUnits && st < nsteps)
+                *reinterpret_cast<float4 *>(lds + 4 * unit) = InQuad<TIn>::f32(buf[u]);
+        }
+    }
+};
+
+}  // namespace wkv7

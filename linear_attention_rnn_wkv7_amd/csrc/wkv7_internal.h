@@ -1,0 +1,43 @@
+// Host-side launch interface between the C ABI (wkv7_abi.cpp) and the
+// kernels.  Shapes and pointers reaching these functions are validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wkv7 {
+
+// Sub-chunk length of the backward's in-register recompute.
+constexpr int kSubChunk = 8;
+
+struct FwdLaunch {
+    const void *in[6];       // r, w, k, v, a, b
+    const float *s0;         // may be null (zeros)
+    float *y, *sT, *ckpt;    // each may be null (skipped)
+    int64_t B, T, H, N;
+    int dtype;               // 0 f32, 1 bf16
+    int chunk;               // checkpoint interval
+};
+
+struct BwdLaunch {
+    const void *in[7];       // r, w, k, v, a, b, dy
+    const float *ckpt;       // required
+    const float *dsT;        // may be null (zeros)
+    float *grad[6];          // dr, dw, dk, dv, da, db
+    float *ds0;              // may be null
+    float *sub;              // sub-checkpoint scratch (see sub_bytes)
+    int64_t B, T, H, N;
+    int dtype;
+    int chunk;
+};
+
+// Bytes of sub-checkpoint scratch the backward needs for a shape.
+size_t sub_bytes(int64_t B, int64_t H, int64_t N, int chunk);
+
+hipError_t launch_forward(const FwdLaunch &a, hipStream_t stream);
+hipError_t launch_backward(const BwdLaunch &a, hipStream_t stream);
+// dst[i] = src ? src[i] : 0 for i < n.
+hipError_t launch_fill(float *dst, const float *src, size_t n, hipStream_t stream);
+
+}  // namespace wkv7

@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments before enqueuing anything.
+Every call here returns from validation (no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from linear_attention_rnn_wkv7_amd import _lib, api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wkv7.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(wkv7_[a-z_0-9]+)\s*\(", src))
+
+
+def test_exports_every_declared_symbol():
+    L = _lib.lib()
+    declared = _declared()
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.wkv7_abi_version() == 100
+
+
+def _shape(B=2, T=10, H=3, N=64, dtype=0, chunk=64):
+    return _lib.Shape(B, T, H, N, dtype, chunk)
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def _fwd(sh, ptrs=None, misalign=None):
+    p = [ctypes.c_void_p(FAKE)] * 6 if ptrs is None else ptrs
+    p = list(p) + [None, None, None, None]
+    if misalign is not None:
+        p[misalign] = ctypes.c_void_p(FAKE + 4)
+    return _lib.lib().wkv7_forward(ctypes.byref(sh) if sh is not None else None, *p, None)
+
+
+def test_forward_validation():
+    ok_ptrs = [ctypes.c_void_p(FAKE)] * 6
+    assert _fwd(None) == _lib.WKV7_ERR_INVALID
+    assert _fwd(_shape(N=32)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert _fwd(_shape(N=128)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert _fwd(_shape(N=0)) == _lib.WKV7_ERR_INVALID
+    assert _fwd(_shape(B=-1)) == _lib.WKV7_ERR_INVALID
+    assert _fwd(_shape(T=-5)) == _lib.WKV7_ERR_INVALID
+    assert _fwd(_shape(dtype=2)) == _lib.WKV7_ERR_INVALID
+    for c in (4, 12, 4104, -8):
+        assert _fwd(_shape(chunk=c)) == _lib.WKV7_ERR_INVALID, c
+    for i in range(6):
+        ptrs = list(ok_ptrs)
+        ptrs[i] = None
+        assert _fwd(_shape(), ptrs) == _lib.WKV7_ERR_INVALID
+    for i in range(10):
+        assert _fwd(_shape(), ok_ptrs, misalign=i) == _lib.WKV7_ERR_INVALID
+    # size overflow
+    assert _fwd(_shape(B=1 << 40, T=1 << 30)) == _lib.WKV7_ERR_INVALID
+    # B*H == 0 is a no-op: succeeds without touching any pointer
+    assert _fwd(_shape(B=0), [None] * 6) == _lib.WKV7_OK
+    assert _fwd(_shape(H=0), [None] * 6) == _lib.WKV7_OK
+
+
+def _bwd(sh, ws=None, ws_bytes=0, ckpt=None, null_at=None, misalign_at=None):
+    p = [ctypes.c_void_p(FAKE)] * 17
+    p[6] = None                        # s0
+    p[8] = None                        # dsT
+    p[9] = ckpt                        # ckpt
+    p[16] = None                       # ds0
+    if null_at is not None:
+        p[null_at] = None
+    if misalign_at is not None:
+        p[misalign_at] = ctypes.c_void_p(FAKE + 8)
+    return _lib.lib().wkv7_backward(ctypes.byref(sh), *p, ws, ws_bytes, None)
+
+
+def test_backward_validation():
+    sh = _shape()
+    for i in (0, 1, 2, 3, 4, 5, 7, 10, 11, 12, 13, 14, 15):   # required pointers
+        assert _bwd(sh, null_at=i) == _lib.WKV7_ERR_INVALID, i
+    for i in range(17):
+        assert _bwd(sh, misalign_at=i) == _lib.WKV7_ERR_INVALID, i
+    assert _bwd(_shape(N=16, dtype=5)) == _lib.WKV7_ERR_INVALID
+    # workspace missing / too small / misaligned
+    assert _bwd(sh) == _lib.WKV7_ERR_WORKSPACE
+    need = _lib.lib().wkv7_backward_workspace_bytes(ctypes.byref(sh), 0)
+    assert _bwd(sh, ctypes.c_void_p(FAKE), need - 1) == _lib.WKV7_ERR_WORKSPACE
+    assert _bwd(sh, ctypes.c_void_p(FAKE + 16), need) == _lib.WKV7_ERR_WORKSPACE
+    need_ck = _lib.lib().wkv7_backward_workspace_bytes(ctypes.byref(sh), 1)
+    assert _bwd(sh, ctypes.c_void_p(FAKE), need_ck - 1,
+                ckpt=ctypes.c_void_p(FAKE)) == _lib.WKV7_ERR_WORKSPACE
+    assert _bwd(_shape(B=0)) == _lib.WKV7_OK
+
+
+def test_size_queries():
+    L = _lib.lib()
+    sh = _shape(B=8, T=4096, H=32, N=64)
+    assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == 8 * 32 * 64 * 64 * 64 * 4
+    # 7 sub-checkpoint slots of one chunk per (b, h)
+    assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) == 8 * 32 * 7 * 64 * 64 * 4
+    ck = 8 * 32 * 64 * 64 * 64 * 4
+    assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 0) == 8 * 32 * 7 * 64 * 64 * 4 + ck
+    sh = _shape(B=1, T=65, H=1, N=16, chunk=8)
+    assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == 9 * 16 * 16 * 4
+    assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) == 0
+    assert L.wkv7_checkpoint_bytes(ctypes.byref(_shape(N=48))) == 0
+    assert L.wkv7_checkpoint_bytes(None) == 0
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4):
+        assert _lib.status_text(code)
+    assert _lib.status_text(-99) == "unknown status"
+
+
+def test_binding_rejects_host_tensors():
+    x = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError):
+        api.wkv7_forward(x, x, x, x, x, x)
+    with pytest.raises(ValueError):
+        api.wkv7_backward(x, x, x, x, x, x, x)
