@@ -14,7 +14,6 @@ vector peak.  `cpu_baseline` times the fp64 oracle on a bounded sample of
 whole (b, h) recurrences of the same workload on the host's cores.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -28,8 +27,6 @@ PEAK_FP32_VALU = 157.3e12   # MI355X published fp32 vector peak (FLOP/s)
 PEAK_HBM = 8.0e12           # MI355X HBM3E (B/s)
 DEFAULT_WORKLOAD = "b8_t4096_h32_n64"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("linear_attention_rnn_wkv7_amd/csrc/wkv7_bwd.hip",
-                  "linear_attention_rnn_wkv7_amd/csrc/wkv7_device.h")
 
 
 def algorithmic(wl):
@@ -45,14 +42,6 @@ def algorithmic(wl):
     return fwd_flops, bwd_flops, fwd_bytes, bwd_bytes
 
 
-def kernel_sha():
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(workload):
     """HBM bytes per backward launch from committed rocprofv3 counter runs,
     or None when absent or taken on a different kernel source."""
@@ -61,6 +50,8 @@ def measured_traffic(workload):
         return None
     with open(path) as f:
         rec = json.load(f)
+    from linear_attention_rnn_wkv7_amd.profiling import kernel_sha
+
     if rec.get("kernel_sha") != kernel_sha():
         return None
     return rec.get("bytes_per_launch")
@@ -100,7 +91,6 @@ def cpu_baseline(inp, wl, budget_s):
     probe_t, _ = run(all_pairs[:1])
     # one pair per core per round; as many pairs as fit the time budget
     n = int(max(1, min(len(all_pairs), cores * max(1, int(budget_s / max(probe_t, 1e-3))))))
-    n = min(n, cores * 4)
     pairs = all_pairs[:n]
     dt, threads = run(pairs)
     token_heads = len(pairs) * wl.T
@@ -123,6 +113,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after timing, run a plain device copy of this many bytes (the "
+                         "reference point for the HBM traffic counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -216,6 +209,13 @@ def main():
         "bwd_ms": bwd_ms,
         "fwd_bwd_roofline_frac": t_roof / (ms * 1e-3),
     }
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, device=dev, dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_bytes"] = args.copy_bytes
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
     print(json.dumps(rec), flush=True)

@@ -1,9 +1,13 @@
-"""ctypes view of libwkv7.so (declarations mirror include/wkv7.h)."""
+"""ctypes view of libwkv7.so (declarations mirror include/wkv7.h).
+
+WKV7_LIB, when set, names another build of the library to load instead of
+the in-tree one (for A/B timing of builds); it must exist.
+"""
 import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libwkv7.so")
+LIB_PATH = os.environ.get("WKV7_LIB") or os.path.join(PKG, "libwkv7.so")
 
 WKV7_F32, WKV7_BF16 = 0, 1
 WKV7_OK, WKV7_ERR_INVALID, WKV7_ERR_UNSUPPORTED, WKV7_ERR_WORKSPACE, WKV7_ERR_HIP = 0, -1, -2, -3, -4

@@ -75,8 +75,11 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
     using Gm = BwdGeom<N>;
     constexpr int R = Gm::R, CC = Gm::CC, LPR = Gm::LPR, RW = Gm::RW, NW = Gm::NW;
     constexpr int NT = Gm::NT, KS = Gm::KS, NV = Gm::NV, NQ = Gm::NQ;
-    __shared__ __align__(16) float stg[2][NV][KS][N];
-    __shared__ __align__(16) float part[KS][NQ][NW][N];
+    constexpr int kSA = NV;            // extra LDS slot: regenerated sa per step
+    // stg[buf][vector][step][n]: the 7 staged inputs plus sa
+    __shared__ __align__(16) float stg[2][NV + 1][KS][N];
+    __shared__ __align__(16) float part[KS][NQ][NW][N];   // per-wave column sums
+    __shared__ __align__(16) float dvb[KS][N];            // dv per step and row
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cg = lane % LPR, rg = lane / LPR;
@@ -144,33 +147,146 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
         x[0] = v4.x; x[1] = v4.y; x[2] = v4.z; x[3] = v4.w;
     };
     auto row_vals = [&](const float *Ls, int q, float (&x)[R]) {
+        if constexpr (R == 4) {
+            const float4 v4 = *reinterpret_cast<const float4 *>(Ls + q * KS * N + row0);
+            x[0] = v4.x; x[1] = v4.y; x[2] = v4.z; x[3] = v4.w;
+        } else {
 #pragma unroll
-        for (int e = 0; e < R; ++e) x[e] = Ls[q * KS * N + row0 + e];
+            for (int e = 0; e < R; ++e) x[e] = Ls[q * KS * N + row0 + e];
+        }
     };
-    // One forward step on X in place; returns sa (pre-update S a) per row.
-    auto fwd_step = [&](const float *Ls, float (&X)[R][CC], float (&sa)[R]) {
-        float va[CC], vw[CC], vk[CC], vb[CC], vv[R];
-        col_vals(Ls, kA, va);
-        col_vals(Ls, kW, vw);
-        col_vals(Ls, kK, vk);
-        col_vals(Ls, kB, vb);
-        row_vals(Ls, kV, vv);
+    auto row_store = [&](float *dst, const float (&x)[R]) {
+        // every lane of the row group writes the same values (no branch)
+        if constexpr (R == 4)
+            *reinterpret_cast<float4 *>(dst + row0) = make_float4(x[0], x[1], x[2], x[3]);
+        else
+#pragma unroll
+            for (int e = 0; e < R; ++e) dst[row0 + e] = x[e];
+    };
+
+    // ---- forward replay of one step
+    struct FwdVals {
+        float a[CC], w[CC], k[CC], b[CC], v[R];
+    };
+    auto load_fwd = [&](const float *Ls, FwdVals &x) {
+        col_vals(Ls, kA, x.a);
+        col_vals(Ls, kW, x.w);
+        col_vals(Ls, kK, x.k);
+        col_vals(Ls, kB, x.b);
+        row_vals(Ls, kV, x.v);
+    };
+    // X <- X diag(w) + v k^T + sa b^T in place; returns sa = X a (pre-update)
+    auto fwd_step = [&](const FwdVals &x, float (&X)[R][CC], float (&sa)[R]) {
+        float u[R][CC];
 #pragma unroll
         for (int e = 0; e < R; ++e) {
-            float acc = 0.f;
+            float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-            for (int c = 0; c < CC; ++c) acc = fmaf(X[e][c], va[c], acc);
-            sa[e] = group_allreduce<LPR>(acc);
+            for (int c = 0; c < CC; c += 2) {
+                a0 = fmaf(X[e][c], x.a[c], a0);
+                a1 = fmaf(X[e][c + 1], x.a[c + 1], a1);
+            }
+#pragma unroll
+            for (int c = 0; c < CC; ++c) u[e][c] = fmaf(X[e][c], x.w[c], x.v[e] * x.k[c]);
+            sa[e] = group_allreduce<LPR>(a0 + a1);
         }
 #pragma unroll
         for (int e = 0; e < R; ++e)
 #pragma unroll
-            for (int c = 0; c < CC; ++c)
-                X[e][c] = fmaf(X[e][c], vw[c], fmaf(vv[e], vk[c], sa[e] * vb[c]));
+            for (int c = 0; c < CC; ++c) X[e][c] = fmaf(sa[e], x.b[c], u[e][c]);
+    };
+
+    // ---- one reverse step
+    struct RevVals {
+        float r[CC], w[CC], k[CC], a[CC], b[CC], v[R], dy[R], sa[R];
+    };
+    auto load_rev = [&](const float *Ls, RevVals &x) {
+        col_vals(Ls, kR, x.r);
+        col_vals(Ls, kW, x.w);
+        col_vals(Ls, kK, x.k);
+        col_vals(Ls, kA, x.a);
+        col_vals(Ls, kB, x.b);
+        row_vals(Ls, kV, x.v);
+        row_vals(Ls, kDY, x.dy);
+        row_vals(Ls, kSA, x.sa);
+    };
+    float G[R][CC];
+    // Pj: state before step j; Pn: state after it.  Leaves the column
+    // partials in part[j] and dv in dvb[j]; carries G to step j-1.
+    auto rev_step = [&](int j, const RevVals &x, const float (&Pj)[R][CC],
+                        const float (&Pn)[R][CC]) {
+        float cq[NQ][CC];
+        // read-out: G += dy r^T; dr from the post-step state
+#pragma unroll
+        for (int c = 0; c < CC; ++c) {
+            float pdr = 0.f;
+#pragma unroll
+            for (int e = 0; e < R; ++e) {
+                pdr = fmaf(Pn[e][c], x.dy[e], pdr);
+                G[e][c] = fmaf(x.dy[e], x.r[c], G[e][c]);
+            }
+            cq[qDR][c] = pdr;
+        }
+        // row dots dsa = G b (needed for the carry) and dv = G k
+        float dsa[R], dvv[R];
+#pragma unroll
+        for (int e = 0; e < R; ++e) {
+            float s0 = 0.f, s1 = 0.f, v0 = 0.f, v1 = 0.f;
+#pragma unroll
+            for (int c = 0; c < CC; c += 2) {
+                s0 = fmaf(G[e][c], x.b[c], s0);
+                s1 = fmaf(G[e][c + 1], x.b[c + 1], s1);
+                v0 = fmaf(G[e][c], x.k[c], v0);
+                v1 = fmaf(G[e][c + 1], x.k[c + 1], v1);
+            }
+            dsa[e] = s0 + s1;
+            dvv[e] = v0 + v1;
+        }
+#pragma unroll
+        for (int e = 0; e < R; ++e) dsa[e] = group_allreduce<LPR>(dsa[e]);
+        // column partials that do not need dsa, and the carry's G*w part
+        float gw[R][CC];
+#pragma unroll
+        for (int c = 0; c < CC; ++c) {
+            float xk = 0.f, xb = 0.f, xw = 0.f;
+#pragma unroll
+            for (int e = 0; e < R; ++e) {
+                xk = fmaf(G[e][c], x.v[e], xk);
+                xb = fmaf(G[e][c], x.sa[e], xb);
+                xw = fmaf(G[e][c], Pj[e][c], xw);
+                gw[e][c] = G[e][c] * x.w[c];
+            }
+            cq[qDK][c] = xk;
+            cq[qDB][c] = xb;
+            cq[qDW][c] = xw;
+        }
+#pragma unroll
+        for (int e = 0; e < R; ++e) dvv[e] = group_allreduce<LPR>(dvv[e]);
+        // in-context term and carry to t-1: G <- G diag(w) + dsa a^T
+#pragma unroll
+        for (int c = 0; c < CC; ++c) {
+            float xa = 0.f;
+#pragma unroll
+            for (int e = 0; e < R; ++e) {
+                xa = fmaf(dsa[e], Pj[e][c], xa);
+                G[e][c] = fmaf(dsa[e], x.a[c], gw[e][c]);
+            }
+            cq[qDA][c] = xa;
+        }
+        // column sums across the row groups of the wave
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const float u0 = swap_add32(cq[q][0], cq[q][2]);
+            const float u1 = swap_add32(cq[q][1], cq[q][3]);
+            float xs = swap_add16(u0, u1);
+            if constexpr (LPR <= 8) xs += dpp<kDppRor8>(xs);
+            if constexpr (LPR <= 4) xs += dpp<kDppRor4>(xs);
+            if (cwriter) part[j][q][wave][ccol] = xs;
+        }
+        row_store(&dvb[j][0], dvv);
     };
 
     // ---- seed G with dsT
-    float G[R][CC];
     if (p.dsT) {
         load_block(p.dsT + bh * NN, G);
     } else {
@@ -183,9 +299,9 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
     Stager<TIn, NV, KS, N, NT> stage;
     float S[R][CC], Snext[R][CC];
     Item it = first_of(p.nck - 1);
-    stage.issue(p.in, vbase + t_begin(it) * stride, stride, n_steps(it), tid);
+    stage.issue(p.in, vbase + t_begin(it) * stride, stride, n_steps(it), wave, lane);
     load_block(state_src(it), S);
-    stage.commit(&stg[0][0][0][0], n_steps(it), tid);
+    stage.commit(&stg[0][0][0][0], n_steps(it), wave, lane);
     __syncthreads();
     int buf = 0;
 
@@ -193,153 +309,109 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
         const Item nx = next_of(it);
         const bool have_next = nx.c >= 0;
         const bool nx_load = have_next && loads_state(nx);
-        if (have_next) stage.issue(p.in, vbase + t_begin(nx) * stride, stride, n_steps(nx), tid);
+        if (have_next) stage.issue(p.in, vbase + t_begin(nx) * stride, stride, n_steps(nx), wave, lane);
         if (nx_load) load_block(state_src(nx), Snext);
         const float *L = &stg[buf][0][0][0];
+        float *Lsa = &stg[buf][kSA][0][0];
         const int nst = n_steps(it);
         const int64_t tb = t_begin(it);
 
         if (!it.B) {
-            // ---- pass A: replay KS steps, then leave a sub-checkpoint when a
-            // later pass-B item will start from it.
+            // ---- pass A (always a full sub-chunk): replay KS steps, then
+            // leave a sub-checkpoint when a later pass-B item starts there.
+            FwdVals fv[2];
+            load_fwd(L, fv[0]);
 #pragma unroll
             for (int j = 0; j < KS; ++j) {
+                if (j + 1 < KS) load_fwd(L + (j + 1) * N, fv[(j + 1) & 1]);
                 float sa[R];
-                fwd_step(L + j * N, S, sa);
+                fwd_step(fv[j & 1], S, sa);
             }
             if (it.s + 1 <= nsub_of(it.c) - 2)
                 store_block(p.sub + (bh * p.nsubw + it.s) * NN, S);
         } else {
-            // ---- pass B: regenerate the sub-chunk's states into registers
+            // ---- pass B: regenerate the sub-chunk's KS + 1 states into
+            // registers (sa of each step goes to its LDS slot) ...
             float P[KS + 1][R][CC];
-            float sav[KS][R];
 #pragma unroll
             for (int e = 0; e < R; ++e)
 #pragma unroll
                 for (int c = 0; c < CC; ++c) P[0][e][c] = S[e][c];
+            if (nst == KS) {
+                FwdVals fv[2];
+                load_fwd(L, fv[0]);
 #pragma unroll
-            for (int j = 0; j < KS; ++j) {
-                if (j < nst) {
+                for (int j = 0; j < KS; ++j) {
+                    if (j + 1 < KS) load_fwd(L + (j + 1) * N, fv[(j + 1) & 1]);
 #pragma unroll
                     for (int e = 0; e < R; ++e)
 #pragma unroll
                         for (int c = 0; c < CC; ++c) P[j + 1][e][c] = P[j][e][c];
-                    fwd_step(L + j * N, P[j + 1], sav[j]);
+                    float sa[R];
+                    fwd_step(fv[j & 1], P[j + 1], sa);
+                    row_store(Lsa + j * N, sa);
                 }
-            }
-            // ---- reverse steps
+                // ... then run the KS reverse steps on them
+                RevVals rv[2];
+                load_rev(L + (KS - 1) * N, rv[(KS - 1) & 1]);
 #pragma unroll
-            for (int j = KS - 1; j >= 0; --j) {
-                if (j >= nst) continue;
-                const float *Ls = L + j * N;
-                float vr[CC], vw[CC], vk[CC], va[CC], vb[CC], vv[R], vdy[R];
-                col_vals(Ls, kR, vr);
-                col_vals(Ls, kW, vw);
-                col_vals(Ls, kK, vk);
-                col_vals(Ls, kA, va);
-                col_vals(Ls, kB, vb);
-                row_vals(Ls, kV, vv);
-                row_vals(Ls, kDY, vdy);
-
-                // read-out: G += dy r^T; dr partial from the post-step state
-                float cq[NQ][CC];
+                for (int j = KS - 1; j >= 0; --j) {
+                    if (j > 0) load_rev(L + (j - 1) * N, rv[(j - 1) & 1]);
+                    rev_step(j, rv[j & 1], P[j], P[j + 1]);
+                }
+            } else {
+                // tail of the sequence: fewer than KS steps
 #pragma unroll
-                for (int c = 0; c < CC; ++c) {
-                    float pdr = 0.f;
+                for (int j = 0; j < KS; ++j) {
+                    if (j < nst) {
+                        FwdVals fv;
+                        load_fwd(L + j * N, fv);
 #pragma unroll
-                    for (int e = 0; e < R; ++e) {
-                        pdr = fmaf(P[j + 1][e][c], vdy[e], pdr);
-                        G[e][c] = fmaf(vdy[e], vr[c], G[e][c]);
+                        for (int e = 0; e < R; ++e)
+#pragma unroll
+                            for (int c = 0; c < CC; ++c) P[j + 1][e][c] = P[j][e][c];
+                        float sa[R];
+                        fwd_step(fv, P[j + 1], sa);
+                        row_store(Lsa + j * N, sa);
                     }
-                    cq[qDR][c] = pdr;
                 }
-                // update gradients
-                float dvp[R], dsap[R];
 #pragma unroll
-                for (int e = 0; e < R; ++e) {
-                    float x = 0.f, y = 0.f;
-#pragma unroll
-                    for (int c = 0; c < CC; ++c) {
-                        x = fmaf(G[e][c], vk[c], x);
-                        y = fmaf(G[e][c], vb[c], y);
+                for (int j = KS - 1; j >= 0; --j) {
+                    if (j < nst) {
+                        RevVals rv;
+                        load_rev(L + j * N, rv);
+                        rev_step(j, rv, P[j], P[j + 1]);
                     }
-                    dvp[e] = x;
-                    dsap[e] = y;
-                }
-#pragma unroll
-                for (int c = 0; c < CC; ++c) {
-                    float xk = 0.f, xb = 0.f, xw = 0.f;
-#pragma unroll
-                    for (int e = 0; e < R; ++e) {
-                        xk = fmaf(G[e][c], vv[e], xk);
-                        xb = fmaf(G[e][c], sav[j][e], xb);
-                        xw = fmaf(G[e][c], P[j][e][c], xw);
-                    }
-                    cq[qDK][c] = xk;
-                    cq[qDB][c] = xb;
-                    cq[qDW][c] = xw;
-                }
-                float dsa[R], dvv[R];
-#pragma unroll
-                for (int e = 0; e < R; ++e) {
-                    dsa[e] = group_allreduce<LPR>(dsap[e]);
-                    dvv[e] = group_allreduce<LPR>(dvp[e]);
-                }
-                // in-context term and carry to t-1
-#pragma unroll
-                for (int c = 0; c < CC; ++c) {
-                    float x = 0.f;
-#pragma unroll
-                    for (int e = 0; e < R; ++e) {
-                        x = fmaf(dsa[e], P[j][e][c], x);
-                        G[e][c] = fmaf(G[e][c], vw[c], dsa[e] * va[c]);
-                    }
-                    cq[qDA][c] = x;
-                }
-                // column sums across the row groups of the wave
-                float cs[NQ];
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) {
-                    const float u0 = swap_add32(cq[q][0], cq[q][2]);
-                    const float u1 = swap_add32(cq[q][1], cq[q][3]);
-                    float x = swap_add16(u0, u1);
-                    if constexpr (LPR <= 8) x += dpp<kDppRor8>(x);
-                    if constexpr (LPR <= 4) x += dpp<kDppRor4>(x);
-                    cs[q] = x;
-                }
-                if (cwriter) {
-#pragma unroll
-                    for (int q = 0; q < NQ; ++q) part[j][q][wave][ccol] = cs[q];
-                }
-                if (cg == 0) {
-                    float *dst = p.dv + vbase + (tb + j) * stride + row0;
-                    if constexpr (R == 4)
-                        *reinterpret_cast<float4 *>(dst) = make_float4(dvv[0], dvv[1], dvv[2], dvv[3]);
-                    else
-#pragma unroll
-                        for (int e = 0; e < R; ++e) dst[e] = dvv[e];
                 }
             }
             __syncthreads();
-            // ---- column outputs of the sub-chunk: fixed-order sum over waves
-            for (int idx = tid; idx < nst * NQ * N; idx += NT) {
+            // ---- outputs of the sub-chunk: the column sums (fixed-order sum
+            // over waves) and dv, written row-contiguous per step
+            for (int idx = tid; idx < nst * (NQ + 1) * N; idx += NT) {
                 const int col = idx % N;
-                const int q = (idx / N) % NQ;
-                const int j = idx / (N * NQ);
-                float x = part[j][q][0][col];
+                const int q = (idx / N) % (NQ + 1);
+                const int j = idx / (N * (NQ + 1));
+                float xo;
+                float *dst;
+                if (q == NQ) {
+                    xo = dvb[j][col];
+                    dst = p.dv;
+                } else {
+                    xo = part[j][q][0][col];
 #pragma unroll
-                for (int w = 1; w < NW; ++w) x += part[j][q][w][col];
-                float *dst = p.dr;
-                if (q == qDK) dst = p.dk;
-                if (q == qDB) dst = p.db;
-                if (q == qDW) dst = p.dw;
-                if (q == qDA) dst = p.da;
-                dst[vbase + (tb + j) * stride + col] = x;
+                    for (int w = 1; w < NW; ++w) xo += part[j][q][w][col];
+                    dst = p.dr;
+                    if (q == qDK) dst = p.dk;
+                    if (q == qDB) dst = p.db;
+                    if (q == qDW) dst = p.dw;
+                    if (q == qDA) dst = p.da;
+                }
+                dst[vbase + (tb + j) * stride + col] = xo;
             }
         }
 
         if (have_next) {
-            stage.commit(&stg[buf ^ 1][0][0][0], n_steps(nx), tid);
+            stage.commit(&stg[buf ^ 1][0][0][0], n_steps(nx), wave, lane);
             if (nx_load) {
 #pragma unroll
                 for (int e = 0; e < R; ++e)

@@ -83,49 +83,85 @@ struct InQuad<uint16_t> {   // bf16 stored as raw 16-bit patterns
 template <typename TIn, int NV>
 struct VecPtrs {
     const TIn *p[NV];
-    // Pointer of vector q (q may differ per lane): a select chain over kernel
-    // arguments, so no pointer array is indexed dynamically.
-    __device__ __forceinline__ const TIn *get(int q) const
-    {
-        const TIn *src = p[0];
-#pragma unroll
-        for (int i = 1; i < NV; ++i)
-            if (q == i) src = p[i];
-        return src;
-    }
 };
 
 // Copies the per-step vectors of one (b, h) for steps [t0, t0 + nsteps) into
 // registers (issue) and then into LDS (commit) as fp32, laid out
 // lds[vec][step][n].  Steps past nsteps are not loaded.
+//
+// The vector index of every load is a compile-time constant and the wave
+// that issues it is fixed per (vector, 64-unit chunk), so each base pointer
+// is a kernel argument held in SGPRs: no pointer is ever chosen per lane
+// (a per-lane choice gets lowered to a dependent load of the pointer).
 template <typename TIn, int NV, int TB, int N, int NTHREADS>
 struct Stager {
-    static constexpr int kUnits = NV * TB * N / 4;
-    static constexpr int kPer = (kUnits + NTHREADS - 1) / NTHREADS;
+    static constexpr int kNW = NTHREADS / kWave;
+    static constexpr int kUnitsPerVec = TB * N / 4;          // 4 elements per unit
+    static_assert(kUnitsPerVec % 32 == 0, "staging granularity");
+    // Chunks of 64 units per vector (a half chunk when 32 units: then two
+    // vectors share one wave instruction, split by lane half).
+    static constexpr int kCPV = kUnitsPerVec >= kWave ? kUnitsPerVec / kWave : 1;
+    static constexpr bool kHalf = kUnitsPerVec < kWave;
+    static constexpr int kSlots = kHalf ? (NV + 1) / 2 : NV * kCPV;   // chunk slots
+    static constexpr int kPer = (kSlots + kNW - 1) / kNW;            // slots per wave
     typename InQuad<TIn>::raw buf[kPer];
 
+    // Slot s holds vector q = s / kCPV, chunk s % kCPV (full chunks), or
+    // vectors 2s and 2s+1 in the two lane halves (half chunks).  Wave w owns
+    // slots w, w + kNW, ...
     __device__ __forceinline__ void issue(const VecPtrs<TIn, NV> &vec, int64_t base_t0,
-                                          int64_t step_stride, int nsteps, int tid)
+                                          int64_t step_stride, int nsteps, int wave, int lane)
     {
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-            const int unit = tid + u * NTHREADS;
-            const int n4 = unit % (N / 4);
-            const int st = (unit / (N / 4)) % TB;
-            const int q = unit / (TB * N / 4);
-            if (unit < kUnits && st < nsteps)
-                buf[u] = InQuad<TIn>::load(vec.get(q) + base_t0 + st * step_stride + 4 * n4);
+        for (int k = 0; k < kPer; ++k) {
+#pragma unroll
+            for (int w = 0; w < kNW; ++w) {
+                const int slot = k * kNW + w;
+                if (slot >= kSlots || wave != w) continue;
+                if constexpr (!kHalf) {
+                    const int q = slot / kCPV;
+                    const int unit = (slot % kCPV) * kWave + lane;
+                    const int st = unit / (N / 4), n4 = unit % (N / 4);
+                    if (st < nsteps)
+                        buf[k] = InQuad<TIn>::load(vec.p[q] + base_t0 + st * step_stride + 4 * n4);
+                } else {
+                    const int q0 = 2 * slot;
+                    const int unit = lane & 31;
+                    const int st = unit / (N / 4), n4 = unit % (N / 4);
+                    const TIn *src = vec.p[q0];
+                    if (q0 + 1 < NV && lane >= 32) src = vec.p[q0 + 1];
+                    const bool valid = st < nsteps && (q0 + 1 < NV || lane < 32);
+                    if (valid)
+                        buf[k] = InQuad<TIn>::load(src + base_t0 + st * step_stride + 4 * n4);
+                }
+            }
         }
     }
 
-    __device__ __forceinline__ void commit(float *lds, int nsteps, int tid)
+    __device__ __forceinline__ void commit(float *lds, int nsteps, int wave, int lane)
     {
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-            const int unit = tid + u * NTHREADS;
-            const int st = (unit / (N / 4)) % TB;
-            if (unit < kUnits && st < nsteps)
-                *reinterpret_cast<float4 *>(lds + 4 * unit) = InQuad<TIn>::f32(buf[u]);
+        for (int k = 0; k < kPer; ++k) {
+#pragma unroll
+            for (int w = 0; w < kNW; ++w) {
+                const int slot = k * kNW + w;
+                if (slot >= kSlots || wave != w) continue;
+                if constexpr (!kHalf) {
+                    const int q = slot / kCPV;
+                    const int unit = (slot % kCPV) * kWave + lane;
+                    const int st = unit / (N / 4);
+                    if (st < nsteps)
+                        *reinterpret_cast<float4 *>(lds + 4 * (q * kUnitsPerVec + unit)) =
+                            InQuad<TIn>::f32(buf[k]);
+                } else {
+                    const int q = 2 * slot + (lane >> 5);
+                    const int unit = lane & 31;
+                    const int st = unit / (N / 4);
+                    if (st < nsteps && q < NV)
+                        *reinterpret_cast<float4 *>(lds + 4 * (q * kUnitsPerVec + unit)) =
+                            InQuad<TIn>::f32(buf[k]);
+                }
+            }
         }
     }
 };

@@ -29,7 +29,7 @@ struct FwdGeom {
     static constexpr int RW = (kWave / LPR) * R;    // rows per wave
     static constexpr int NW = N / RW;               // waves per workgroup
     static constexpr int NT = NW * kWave;
-    static constexpr int TB = 8;                    // steps per staged block
+    static constexpr int TB = 16;                   // steps per staged block
     static constexpr int NV = 6;                    // r, w, k, v, a, b
     static_assert(N % RW == 0 && CC % 4 == 0, "tile");
 };
@@ -79,89 +79,164 @@ wkv7_fwd_kernel(FwdArgs<TIn> p)
             for (int c = 0; c < CC; ++c) S[e][c] = 0.f;
     }
 
-    Stager<TIn, NV, TB, N, NT> stage;
+    // Per-step operands read back from LDS: this lane's CC columns of a, w,
+    // k, b, r and its R entries of v.
+    struct StepVals {
+        float a[CC], w[CC], k[CC], b[CC], r[CC], v[R];
+    };
+    auto load_step = [&](const float *Ls, StepVals &sv) {
+#pragma unroll
+        for (int c = 0; c < CC; c += 4) {
+            const float4 qa = *reinterpret_cast<const float4 *>(Ls + kA * TB * N + col0 + c);
+            const float4 qw = *reinterpret_cast<const float4 *>(Ls + kW * TB * N + col0 + c);
+            const float4 qk = *reinterpret_cast<const float4 *>(Ls + kK * TB * N + col0 + c);
+            const float4 qb = *reinterpret_cast<const float4 *>(Ls + kB * TB * N + col0 + c);
+            const float4 qr = *reinterpret_cast<const float4 *>(Ls + kR * TB * N + col0 + c);
+            sv.a[c] = qa.x; sv.a[c + 1] = qa.y; sv.a[c + 2] = qa.z; sv.a[c + 3] = qa.w;
+            sv.w[c] = qw.x; sv.w[c + 1] = qw.y; sv.w[c + 2] = qw.z; sv.w[c + 3] = qw.w;
+            sv.k[c] = qk.x; sv.k[c + 1] = qk.y; sv.k[c + 2] = qk.z; sv.k[c + 3] = qk.w;
+            sv.b[c] = qb.x; sv.b[c + 1] = qb.y; sv.b[c + 2] = qb.z; sv.b[c + 3] = qb.w;
+            sv.r[c] = qr.x; sv.r[c + 1] = qr.y; sv.r[c + 2] = qr.z; sv.r[c + 3] = qr.w;
+        }
+#pragma unroll
+        for (int e = 0; e < R; ++e) sv.v[e] = Ls[kV * TB * N + row0 + e];
+    };
+    // One step on S; returns this lane's rows of y (already summed).
+    auto do_step = [&](const StepVals &sv, float (&yv)[R]) {
+        float sa[R], u[R][CC];
+#pragma unroll
+        for (int e = 0; e < R; ++e) {
+            // sa = S a over the pre-update state: two partial chains, then
+            // the sum over the row group.
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int c = 0; c < CC; c += 2) {
+                a0 = fmaf(S[e][c], sv.a[c], a0);
+                a1 = fmaf(S[e][c + 1], sv.a[c + 1], a1);
+            }
+            // the part of the update that does not need sa
+#pragma unroll
+            for (int c = 0; c < CC; ++c) u[e][c] = fmaf(S[e][c], sv.w[c], sv.v[e] * sv.k[c]);
+            sa[e] = group_allreduce<LPR>(a0 + a1);
+        }
+        // S <- S diag(w) + v k^T + sa b^T ; y = S r over the updated state
+#pragma unroll
+        for (int e = 0; e < R; ++e) {
+            float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+            for (int c = 0; c < CC; c += 2) {
+                S[e][c] = fmaf(sa[e], sv.b[c], u[e][c]);
+                S[e][c + 1] = fmaf(sa[e], sv.b[c + 1], u[e][c + 1]);
+                y0 = fmaf(S[e][c], sv.r[c], y0);
+                y1 = fmaf(S[e][c + 1], sv.r[c + 1], y1);
+            }
+            yv[e] = group_allreduce<LPR>(y0 + y1);
+        }
+    };
+
+    // Input staging runs two blocks ahead: while block b computes from LDS,
+    // block b+1 sits in registers (loaded during block b-1) and block b+2 is
+    // being loaded.  stage[x & 1] holds block x.
+    using StagerT = Stager<TIn, NV, TB, N, NT>;
+    StagerT stage0, stage1;
     const int64_t nblk = (T + TB - 1) / TB;
+    auto steps_of = [&](int64_t blk) -> int {
+        const int64_t rem = T - blk * TB;
+        return (int)(rem < TB ? rem : TB);
+    };
     if (nblk > 0) {
-        const int n0 = (int)(T < TB ? T : TB);
-        stage.issue(p.in, vbase, stride, n0, tid);
-        stage.commit(&lds[0][0][0][0], n0, tid);
+        stage0.issue(p.in, vbase, stride, steps_of(0), wave, lane);
+        if (nblk > 1) stage1.issue(p.in, vbase + TB * stride, stride, steps_of(1), wave, lane);
+        stage0.commit(&lds[0][0][0][0], steps_of(0), wave, lane);
     }
     __syncthreads();
 
-    for (int64_t blk = 0; blk < nblk; ++blk) {
-        const int64_t t0 = blk * TB;
-        const int nst = (int)((T - t0) < TB ? (T - t0) : TB);
-        const bool more = blk + 1 < nblk;
-        const int nnext = more ? (int)((T - t0 - TB) < TB ? (T - t0 - TB) : TB) : 0;
-        if (more) stage.issue(p.in, vbase + (t0 + TB) * stride, stride, nnext, tid);
-
-        // Checkpoint: the state before step t0 when t0 starts a chunk (the
-        // chunk is a multiple of TB, so this is the only step it can be).
-        if (p.ckpt && t0 % p.chunk == 0) {
-            float *dst = p.ckpt + (bh * p.nck + t0 / p.chunk) * N * N + (int64_t)row0 * N + col0;
+    // Checkpoints: the state before every step that is a multiple of the
+    // chunk (a multiple of 8, so within a block only offsets 0 and 8).
+    static_assert(TB == 16, "checkpoint offsets assume 16-step blocks");
+    int64_t next_ck = 0, ck_slot = 0;
+    auto maybe_checkpoint = [&](int64_t t) {
+        if (t == next_ck) {
+            if (p.ckpt) {
+                float *dst = p.ckpt + (bh * p.nck + ck_slot) * N * N + (int64_t)row0 * N + col0;
 #pragma unroll
-            for (int e = 0; e < R; ++e)
+                for (int e = 0; e < R; ++e)
 #pragma unroll
-                for (int c = 0; c < CC; c += 4)
-                    *reinterpret_cast<float4 *>(dst + e * N + c) =
-                        make_float4(S[e][c], S[e][c + 1], S[e][c + 2], S[e][c + 3]);
+                    for (int c = 0; c < CC; c += 4)
+                        *reinterpret_cast<float4 *>(dst + e * N + c) =
+                            make_float4(S[e][c], S[e][c + 1], S[e][c + 2], S[e][c + 3]);
+            }
+            ++ck_slot;
+            next_ck += p.chunk;
         }
+    };
+
+    // One block; `mine` holds this block's registers slot (free now: it was
+    // committed before this block) and `other` holds block blk+1.
+    auto run_block = [&](int64_t blk, StagerT &mine, StagerT &other) {
+        const int64_t t0 = blk * TB;
+        const int nst = steps_of(blk);
+        if (blk + 2 < nblk)
+            mine.issue(p.in, vbase + (t0 + 2 * TB) * stride, stride, steps_of(blk + 2), wave, lane);
 
         const float *L = &lds[blk & 1][0][0][0];
+        float ybuf[TB][R];
+        if (nst == TB) {
+            // steady state: straight-line code except the rare mid-block
+            // checkpoint test; the next step's operands are read from LDS
+            // while the current step computes
+            StepVals sv[2];
+            load_step(L, sv[0]);
 #pragma unroll
-        for (int s = 0; s < TB; ++s) {
-            if (s >= nst) continue;
-            const float *Ls = L + s * N;
-            float va[CC], vw[CC], vk[CC], vb[CC], vr[CC], vv[R];
-#pragma unroll
-            for (int c = 0; c < CC; c += 4) {
-                const float4 qa = *reinterpret_cast<const float4 *>(Ls + kA * TB * N + col0 + c);
-                const float4 qw = *reinterpret_cast<const float4 *>(Ls + kW * TB * N + col0 + c);
-                const float4 qk = *reinterpret_cast<const float4 *>(Ls + kK * TB * N + col0 + c);
-                const float4 qb = *reinterpret_cast<const float4 *>(Ls + kB * TB * N + col0 + c);
-                const float4 qr = *reinterpret_cast<const float4 *>(Ls + kR * TB * N + col0 + c);
-                va[c] = qa.x; va[c + 1] = qa.y; va[c + 2] = qa.z; va[c + 3] = qa.w;
-                vw[c] = qw.x; vw[c + 1] = qw.y; vw[c + 2] = qw.z; vw[c + 3] = qw.w;
-                vk[c] = qk.x; vk[c + 1] = qk.y; vk[c + 2] = qk.z; vk[c + 3] = qk.w;
-                vb[c] = qb.x; vb[c + 1] = qb.y; vb[c + 2] = qb.z; vb[c + 3] = qb.w;
-                vr[c] = qr.x; vr[c + 1] = qr.y; vr[c + 2] = qr.z; vr[c + 3] = qr.w;
+            for (int s = 0; s < TB; ++s) {
+                if (s == 0 || s == 8) maybe_checkpoint(t0 + s);
+                if (s + 1 < TB) load_step(L + (s + 1) * N, sv[(s + 1) & 1]);
+                do_step(sv[s & 1], ybuf[s]);
             }
+        } else {
 #pragma unroll
-            for (int e = 0; e < R; ++e) vv[e] = Ls[kV * TB * N + row0 + e];
-
-            // sa = S a over the pre-update state (row dot, then group sum)
-            float sa[R];
-#pragma unroll
-            for (int e = 0; e < R; ++e) {
-                float acc = 0.f;
-#pragma unroll
-                for (int c = 0; c < CC; ++c) acc = fmaf(S[e][c], va[c], acc);
-                sa[e] = group_allreduce<LPR>(acc);
-            }
-            // S <- S diag(w) + v k^T + sa b^T ; y = S r (post-update)
-            float yv[R];
-#pragma unroll
-            for (int e = 0; e < R; ++e) {
-                float acc = 0.f;
-#pragma unroll
-                for (int c = 0; c < CC; ++c) {
-                    S[e][c] = fmaf(S[e][c], vw[c], fmaf(vv[e], vk[c], sa[e] * vb[c]));
-                    acc = fmaf(S[e][c], vr[c], acc);
+            for (int s = 0; s < TB; ++s) {
+                if (s < nst) {
+                    if (s == 0 || s == 8) maybe_checkpoint(t0 + s);
+                    StepVals sv;
+                    load_step(L + s * N, sv);
+                    do_step(sv, ybuf[s]);
                 }
-                yv[e] = group_allreduce<LPR>(acc);
             }
-            if (p.y && cg == 0) {
-                float *dst = p.y + vbase + (t0 + s) * stride + row0;
-                if constexpr (R == 2)
-                    *reinterpret_cast<float2 *>(dst) = make_float2(yv[0], yv[1]);
-                else
+        }
+        // y of the block: lane cg of each row group writes step cg (+LPR...).
+        if (p.y) {
 #pragma unroll
-                    for (int e = 0; e < R; ++e) dst[e] = yv[e];
+            for (int s0 = 0; s0 < TB; s0 += LPR) {
+                const int s = s0 + cg;
+                float yo[R];
+#pragma unroll
+                for (int e = 0; e < R; ++e) {
+                    yo[e] = ybuf[s0][e];
+#pragma unroll
+                    for (int q = 1; q < LPR && s0 + q < TB; ++q)
+                        if (cg == q) yo[e] = ybuf[s0 + q][e];
+                }
+                if (s < nst) {
+                    float *dst = p.y + vbase + (t0 + s) * stride + row0;
+                    if constexpr (R == 2)
+                        *reinterpret_cast<float2 *>(dst) = make_float2(yo[0], yo[1]);
+                    else
+#pragma unroll
+                        for (int e = 0; e < R; ++e) dst[e] = yo[e];
+                }
             }
         }
 
-        if (more) stage.commit(&lds[(blk + 1) & 1][0][0][0], nnext, tid);
+        if (blk + 1 < nblk)
+            other.commit(&lds[(blk + 1) & 1][0][0][0], steps_of(blk + 1), wave, lane);
         __syncthreads();
+    };
+    for (int64_t blk = 0; blk < nblk; ++blk) {
+        if ((blk & 1) == 0)
+            run_block(blk, stage0, stage1);
+        else
+            run_block(blk, stage1, stage0);
     }
 
     if (p.sT) {

@@ -1,0 +1,125 @@
+"""Summaries of rocprofv3 output for the profiles/ directory.
+
+    python -m linear_attention_rnn_wkv7_amd.profiling stats  --csv K.csv --cmd "..." --out F.md
+    python -m linear_attention_rnn_wkv7_amd.profiling traffic --fetch F.csv --write W.csv \
+        --kernel wkv7_bwd_kernel --copy-bytes N --workload NAME --cmd "..." --out F.json
+
+`stats` condenses a --kernel-trace --stats kernel_stats.csv.  `traffic`
+turns per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of a kernel into bytes per
+launch, scaling each counter by what it reads for the plain device copy of
+`copy-bytes` bytes that bench.py --copy-bytes runs in the same process.
+"""
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = ("linear_attention_rnn_wkv7_amd/csrc/wkv7_bwd.hip",
+                  "linear_attention_rnn_wkv7_amd/csrc/wkv7_fwd.hip",
+                  "linear_attention_rnn_wkv7_amd/csrc/wkv7_device.h")
+
+
+def kernel_sha(sources=KERNEL_SOURCES):
+    h = hashlib.sha256()
+    for rel in sources:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name):
+    for key in ("wkv7_bwd_kernel", "wkv7_fwd_kernel", "fill_kernel", "copy"):
+        if key in name:
+            return key if key != "copy" else name[:60]
+    return name[:60]
+
+
+def stats(csv_path, cmd, out):
+    rows = list(csv.DictReader(open(csv_path)))
+    lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", cmd, "```", "",
+             "| kernel | calls | total ms | average us | min us | max us | % |",
+             "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        if "wkv7" not in name and float(r.get("Percentage", 0)) < 1.0:
+            continue
+        lines.append(f"| `{_short(name)}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    lines.append("")
+    lines.append(f"Kernel sources sha: `{kernel_sha()}`")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out
+
+
+def _per_dispatch(csv_path, counter):
+    vals = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def _pick(vals, substr):
+    hits = [v for k, v in vals.items() if substr in k]
+    if not hits:
+        raise SystemExit(f"no dispatches of {substr}")
+    return statistics.median([x for h in hits for x in h])
+
+
+def traffic(fetch_csv, write_csv, kernel, copy_bytes, workload, cmd, out):
+    f = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    w = _per_dispatch(write_csv, "WRITE_SIZE")
+    copy_key = "copy"                    # torch's elementwise copy kernel
+    f_k, w_k = _pick(f, kernel), _pick(w, kernel)
+    # the copy of known size is the largest copy dispatch (torch also issues
+    # small host<->device copies)
+    f_c = max(x for k, v in f.items() if copy_key in k.lower() for x in v)
+    w_c = max(x for k, v in w.items() if copy_key in k.lower() for x in v)
+    fetch_scale = copy_bytes / (f_c * 1024.0)
+    write_scale = copy_bytes / (w_c * 1024.0)
+    rec = {
+        "workload": workload,
+        "kernel": kernel,
+        "kernel_sha": kernel_sha(),
+        "command": cmd,
+        "fetch_kib_per_dispatch": f_k,
+        "write_kib_per_dispatch": w_k,
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": f_c,
+        "copy_write_kib": w_c,
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "bytes_per_launch": f_k * 1024.0 * fetch_scale + w_k * 1024.0 * write_scale,
+    }
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return rec
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("--csv", required=True)
+    a.add_argument("--cmd", required=True)
+    a.add_argument("--out", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--kernel", default="wkv7_bwd_kernel")
+    b.add_argument("--copy-bytes", type=int, required=True)
+    b.add_argument("--workload", required=True)
+    b.add_argument("--cmd", required=True)
+    b.add_argument("--out", required=True)
+    args = ap.parse_args()
+    if args.what == "stats":
+        print(stats(args.csv, args.cmd, args.out))
+    else:
+        print(json.dumps(traffic(args.fetch, args.write, args.kernel, args.copy_bytes,
+                                 args.workload, args.cmd, args.out)))
