@@ -39,6 +39,8 @@ def algorithmic(wl):
     bwd_flops = 26 * N * N * th
     fwd_bytes = (6 * N * eb + 4 * N + ck) * th    # r,w,k,v,a,b in; y out; ckpt out
     bwd_bytes = (7 * N * eb + 6 * N * 4 + ck) * th  # 7 vectors in; 6 grads out; ckpt in
+    # (the sa tape, 2*4*N more bytes per token-head, is this build's choice
+    # and is not counted as algorithmic)
     return fwd_flops, bwd_flops, fwd_bytes, bwd_bytes
 
 
@@ -137,7 +139,8 @@ def main():
     f32 = torch.float32
     y = torch.empty((B, T, H, N), device=dev, dtype=f32)
     sT = torch.empty((B, H, N, N), device=dev, dtype=f32)
-    ck = torch.empty((B, H, (T + C - 1) // C, N, N), device=dev, dtype=f32)
+    ck = torch.empty(api.wkv7_checkpoint_bytes(B, T, H, N, inp["r"].dtype, C) // 4, device=dev,
+                     dtype=f32)
     grads = {n: torch.empty((B, T, H, N), device=dev, dtype=f32)
              for n in ("dr", "dw", "dk", "dv", "da", "db")}
     grads["ds0"] = torch.empty((B, H, N, N), device=dev, dtype=f32)

@@ -22,8 +22,12 @@
  * Layouts (all row-major, contiguous):
  *   vectors r, w, k, v, a, b, dy, y, dr, dw, dk, dv, da, db : [B][T][H][N]
  *   states  s0, sT, dsT, ds0                                 : [B][H][N][N] fp32
- *   checkpoints ckpt : [B][H][ceil(T/C)][N][N] fp32; slot c holds the state
- *                      before step c*C (slot 0 = s0, or zeros).
+ *   checkpoint record ckpt (wkv7_checkpoint_bytes bytes, fp32):
+ *     states  [B][H][ceil(T/C)][N][N] at offset 0; slot c holds the state
+ *             before step c*C (slot 0 = s0, or zeros);
+ *     sa tape [B][T][H][N] at byte offset roundup(states bytes, 256): the
+ *             forward's sa_t = S_{t-1} a_t, so the backward regenerates
+ *             states without recomputing these dot products.
  * Inputs r..b and dy are fp32 or bf16 (wkv7_shape.dtype); everything else,
  * including y and all gradients, is fp32.
  *
@@ -75,12 +79,12 @@ enum {
     WKV7_ERR_HIP = -4           /* a kernel launch failed */
 };
 
-/* Bytes of the checkpoint buffer for `shape` (B*H*ceil(T/C)*N*N*4); 0 when
- * the shape is invalid or empty. */
+/* Bytes of the checkpoint record for `shape`:
+ * roundup(B*H*ceil(T/C)*N*N*4, 256) + B*T*H*N*4; 0 when the shape is invalid. */
 size_t wkv7_checkpoint_bytes(const wkv7_shape *shape);
 
 /* Bytes of device workspace wkv7_backward needs: the per-(b,h) state
- * sub-checkpoints of one chunk, plus room for the checkpoints themselves
+ * sub-checkpoints of one chunk, plus room for the checkpoint record itself
  * when `ckpt_provided` is 0.  0 when the shape is invalid or empty. */
 size_t wkv7_backward_workspace_bytes(const wkv7_shape *shape, int ckpt_provided);
 
@@ -90,8 +94,8 @@ size_t wkv7_backward_workspace_bytes(const wkv7_shape *shape, int ckpt_provided)
  *   s0   : initial state, fp32 [B][H][N][N]; NULL means zeros.
  *   y    : output, fp32 [B][T][H][N]; NULL skips it.
  *   sT   : final state, fp32 [B][H][N][N]; NULL skips it.
- *   ckpt : checkpoints for wkv7_backward, wkv7_checkpoint_bytes(shape) bytes;
- *          NULL skips them.
+ *   ckpt : checkpoint record for wkv7_backward, wkv7_checkpoint_bytes(shape)
+ *          bytes (states every C steps and the per-step sa); NULL skips it.
  * With T == 0, sT receives s0 (or zeros). */
 int wkv7_forward(const wkv7_shape *shape,
                  const void *r, const void *w, const void *k, const void *v,
@@ -104,8 +108,8 @@ int wkv7_forward(const wkv7_shape *shape,
  *   s0   : the forward's initial state (NULL = zeros); read only when
  *          ckpt is NULL.
  *   dsT  : dL/d(final state), fp32 [B][H][N][N]; NULL means zeros.
- *   ckpt : the checkpoints a wkv7_forward call with the same inputs, s0 and
- *          chunk wrote; NULL makes the backward recompute them into the
+ *   ckpt : the checkpoint record a wkv7_forward call with the same inputs,
+ *          s0 and chunk wrote; NULL makes the backward recompute it into the
  *          workspace first.
  *   dr, dw, dk, dv, da, db : outputs, fp32 [B][T][H][N], all required.
  *   ds0  : dL/ds0, fp32 [B][H][N][N]; NULL skips it.

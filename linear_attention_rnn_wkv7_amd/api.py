@@ -62,6 +62,9 @@ def wkv7_forward(r, w, k, v, a, b, s0=None, *, chunk=64, want_y=True, want_sT=Tr
                  want_ckpt=False, stream=None, out=None):
     """Run the forward scan.  Returns (y, sT, ckpt); unwanted outputs are None.
 
+    ckpt is the flat fp32 checkpoint record (states every `chunk` steps, then
+    the per-step sa) that wkv7_backward consumes.
+
     ``out`` may supply preallocated (y, sT, ckpt) tensors (None entries are
     allocated when wanted)."""
     (B, T, H, N), dt = _check_vecs("rwkvab", (r, w, k, v, a, b))
@@ -73,8 +76,8 @@ def wkv7_forward(r, w, k, v, a, b, s0=None, *, chunk=64, want_y=True, want_sT=Tr
     if want_sT and sT is None:
         sT = torch.empty((B, H, N, N), device=dev, dtype=torch.float32)
     if want_ckpt and ckpt is None:
-        nck = (T + chunk - 1) // chunk
-        ckpt = torch.empty((B, H, nck, N, N), device=dev, dtype=torch.float32)
+        ckpt = torch.empty(wkv7_checkpoint_bytes(B, T, H, N, dt, chunk) // 4, device=dev,
+                           dtype=torch.float32)
     sh = make_shape(B, T, H, N, dt, chunk)
     rc = _lib.lib().wkv7_forward(ctypes.byref(sh), *map(_ptr, (r, w, k, v, a, b, s0)),
                                  _ptr(y if want_y else None), _ptr(sT if want_sT else None),

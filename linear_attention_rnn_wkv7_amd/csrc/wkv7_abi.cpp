@@ -60,9 +60,22 @@ size_t round_up(size_t x)
     return (x + kAlign - 1) / kAlign * kAlign;
 }
 
-size_t ckpt_bytes(const Dims &d)
+// The checkpoint record: the states every C steps, then (at a 256-byte
+// aligned offset) the per-step sa values in the vector layout.
+size_t ckpt_state_bytes(const Dims &d)
 {
     return d.state_elems * (size_t)d.nck * sizeof(float);
+}
+
+size_t ckpt_bytes(const Dims &d)
+{
+    return round_up(ckpt_state_bytes(d)) + d.vec_elems * sizeof(float);
+}
+
+const float *tape_of(const float *ck, const Dims &d)
+{
+    return reinterpret_cast<const float *>(reinterpret_cast<const char *>(ck) +
+                                           round_up(ckpt_state_bytes(d)));
 }
 
 // Sub-checkpoint scratch first, then (when needed) the checkpoints.
@@ -122,6 +135,7 @@ int wkv7_forward(const wkv7_shape *shape, const void *r, const void *w, const vo
     L.y = y;
     L.sT = sT;
     L.ckpt = ckpt;
+    L.satape = ckpt ? const_cast<float *>(tape_of(ckpt, d)) : nullptr;
     L.B = d.B;
     L.T = d.T;
     L.H = d.H;
@@ -176,6 +190,7 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
         F.y = nullptr;
         F.sT = nullptr;
         F.ckpt = own;
+        F.satape = const_cast<float *>(tape_of(own, d));
         F.B = d.B;
         F.T = d.T;
         F.H = d.H;
@@ -189,6 +204,7 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
     wkv7::BwdLaunch L;
     for (int i = 0; i < 7; ++i) L.in[i] = in[i];
     L.ckpt = ck;
+    L.satape = tape_of(ck, d);
     L.dsT = dsT;
     for (int i = 0; i < 6; ++i) L.grad[i] = grad[i];
     L.ds0 = ds0;
@@ -216,7 +232,7 @@ const char *wkv7_status_string(int status)
 
 int wkv7_abi_version(void)
 {
-    return 100;
+    return 101;
 }
 
 }  // extern "C"

@@ -54,6 +54,7 @@ enum { qDR = 0, qDK = 1, qDB = 2, qDW = 3, qDA = 4 };
 template <typename TIn>
 struct BwdArgs {
     VecPtrs<TIn, 7> in;
+    VecPtrs<float, 1> satape;   // the forward's per-step sa, [B][T][H][N]
     const float *ckpt, *dsT;
     float *dr, *dw, *dk, *dv, *da, *db, *ds0;
     float *sub;
@@ -75,11 +76,14 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
     using Gm = BwdGeom<N>;
     constexpr int R = Gm::R, CC = Gm::CC, LPR = Gm::LPR, RW = Gm::RW, NW = Gm::NW;
     constexpr int NT = Gm::NT, KS = Gm::KS, NV = Gm::NV, NQ = Gm::NQ;
-    constexpr int kSA = NV;            // extra LDS slot: regenerated sa per step
+    constexpr int kSA = NV;            // extra LDS slot: sa per step (from the tape)
     // stg[buf][vector][step][n]: the 7 staged inputs plus sa
     __shared__ __align__(16) float stg[2][NV + 1][KS][N];
-    __shared__ __align__(16) float part[KS][NQ][NW][N];   // per-wave column sums
-    __shared__ __align__(16) float dvb[KS][N];            // dv per step and row
+    // per-wave column sums and dv of a pass-B item, double-buffered: item i
+    // writes buffer pb, the next item sums and stores it behind the barrier
+    // that ends item i
+    __shared__ __align__(16) float part[2][KS][NQ][NW][N];
+    __shared__ __align__(16) float dvb[2][KS][N];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cg = lane % LPR, rg = lane / LPR;
@@ -164,36 +168,24 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
             for (int e = 0; e < R; ++e) dst[row0 + e] = x[e];
     };
 
-    // ---- forward replay of one step
+    // ---- forward replay of one step, with sa taken from the forward's tape:
+    // X <- X diag(w) + v k^T + sa b^T in place
     struct FwdVals {
-        float a[CC], w[CC], k[CC], b[CC], v[R];
+        float w[CC], k[CC], b[CC], v[R], sa[R];
     };
     auto load_fwd = [&](const float *Ls, FwdVals &x) {
-        col_vals(Ls, kA, x.a);
         col_vals(Ls, kW, x.w);
         col_vals(Ls, kK, x.k);
         col_vals(Ls, kB, x.b);
         row_vals(Ls, kV, x.v);
+        row_vals(Ls, kSA, x.sa);
     };
-    // X <- X diag(w) + v k^T + sa b^T in place; returns sa = X a (pre-update)
-    auto fwd_step = [&](const FwdVals &x, float (&X)[R][CC], float (&sa)[R]) {
-        float u[R][CC];
-#pragma unroll
-        for (int e = 0; e < R; ++e) {
-            float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-            for (int c = 0; c < CC; c += 2) {
-                a0 = fmaf(X[e][c], x.a[c], a0);
-                a1 = fmaf(X[e][c + 1], x.a[c + 1], a1);
-            }
-#pragma unroll
-            for (int c = 0; c < CC; ++c) u[e][c] = fmaf(X[e][c], x.w[c], x.v[e] * x.k[c]);
-            sa[e] = group_allreduce<LPR>(a0 + a1);
-        }
+    auto fwd_step = [&](const FwdVals &x, float (&X)[R][CC]) {
 #pragma unroll
         for (int e = 0; e < R; ++e)
 #pragma unroll
-            for (int c = 0; c < CC; ++c) X[e][c] = fmaf(sa[e], x.b[c], u[e][c]);
+            for (int c = 0; c < CC; ++c)
+                X[e][c] = fmaf(x.sa[e], x.b[c], fmaf(X[e][c], x.w[c], x.v[e] * x.k[c]));
     };
 
     // ---- one reverse step
@@ -213,7 +205,7 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
     float G[R][CC];
     // Pj: state before step j; Pn: state after it.  Leaves the column
     // partials in part[j] and dv in dvb[j]; carries G to step j-1.
-    auto rev_step = [&](int j, const RevVals &x, const float (&Pj)[R][CC],
+    auto rev_step = [&](int j, int pb, const RevVals &x, const float (&Pj)[R][CC],
                         const float (&Pn)[R][CC]) {
         float cq[NQ][CC];
         // read-out: G += dy r^T; dr from the post-step state
@@ -281,10 +273,45 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
             float xs = swap_add16(u0, u1);
             if constexpr (LPR <= 8) xs += dpp<kDppRor8>(xs);
             if constexpr (LPR <= 4) xs += dpp<kDppRor4>(xs);
-            if (cwriter) part[j][q][wave][ccol] = xs;
+            if (cwriter) part[pb][j][q][wave][ccol] = xs;
         }
-        row_store(&dvb[j][0], dvv);
+        row_store(&dvb[pb][j][0], dvv);
     };
+
+    // ---- outputs of a pass-B item: the column sums (fixed-order sum over
+    // waves) and dv, from LDS buffer fb, for steps [ftb, ftb + fnst)
+    auto finalize = [&](int fb, int64_t ftb, int fnst) {
+        // Unit f covers 4 columns of one (quantity, step) pair; for N = 64
+        // a wave's 64 units span 4 pairs of one quantity.
+        constexpr int kU = (NQ + 1) * KS * (N / 4);
+#pragma unroll
+        for (int k = 0; k < (kU + NT - 1) / NT; ++k) {
+            const int f = tid + k * NT;
+            const int pair = f / (N / 4), c4 = f % (N / 4);
+            int q = pair / KS;
+            const int j = pair % KS;
+            if constexpr (N / 4 * KS % kWave == 0) q = __builtin_amdgcn_readfirstlane(q);
+            if (f < kU && j < fnst) {
+                float4 xo;
+                if (q == NQ) {
+                    xo = *reinterpret_cast<const float4 *>(&dvb[fb][j][4 * c4]);
+                } else {
+                    xo = *reinterpret_cast<const float4 *>(&part[fb][j][q][0][4 * c4]);
+#pragma unroll
+                    for (int w = 1; w < NW; ++w) {
+                        const float4 t = *reinterpret_cast<const float4 *>(&part[fb][j][q][w][4 * c4]);
+                        xo.x += t.x; xo.y += t.y; xo.z += t.z; xo.w += t.w;
+                    }
+                }
+                float *dst = q == qDR ? p.dr : q == qDK ? p.dk : q == qDB ? p.db
+                           : q == qDW ? p.dw : q == qDA ? p.da : p.dv;
+                *reinterpret_cast<float4 *>(dst + vbase + (ftb + j) * stride + 4 * c4) = xo;
+            }
+        }
+    };
+    bool fin_pending = false;
+    int fin_buf = 0, fin_nst = 0, pb = 0;
+    int64_t fin_tb = 0;
 
     // ---- seed G with dsT
     if (p.dsT) {
@@ -296,12 +323,22 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
             for (int c = 0; c < CC; ++c) G[e][c] = 0.f;
     }
 
+    // inputs each item needs: pass A replays with w, k, v, b (+ sa); pass B
+    // also needs r, a, dy
+    constexpr unsigned kMaskA = (1u << kW) | (1u << kK) | (1u << kV) | (1u << kB);
+    constexpr unsigned kMaskB = (1u << NV) - 1u;
     Stager<TIn, NV, KS, N, NT> stage;
+    Stager<float, 1, KS, N, NT> sastage;
     float S[R][CC], Snext[R][CC];
     Item it = first_of(p.nck - 1);
-    stage.issue(p.in, vbase + t_begin(it) * stride, stride, n_steps(it), wave, lane);
-    load_block(state_src(it), S);
-    stage.commit(&stg[0][0][0][0], n_steps(it), wave, lane);
+    {
+        const unsigned m = it.B ? kMaskB : kMaskA;
+        stage.issue(p.in, vbase + t_begin(it) * stride, stride, n_steps(it), wave, lane, m);
+        sastage.issue(p.satape, vbase + t_begin(it) * stride, stride, n_steps(it), wave, lane);
+        load_block(state_src(it), S);
+        stage.commit(&stg[0][0][0][0], n_steps(it), wave, lane, m);
+        sastage.commit(&stg[0][kSA][0][0], n_steps(it), wave, lane);
+    }
     __syncthreads();
     int buf = 0;
 
@@ -309,10 +346,17 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
         const Item nx = next_of(it);
         const bool have_next = nx.c >= 0;
         const bool nx_load = have_next && loads_state(nx);
-        if (have_next) stage.issue(p.in, vbase + t_begin(nx) * stride, stride, n_steps(nx), wave, lane);
+        const unsigned nx_mask = nx.B ? kMaskB : kMaskA;
+        if (have_next) {
+            stage.issue(p.in, vbase + t_begin(nx) * stride, stride, n_steps(nx), wave, lane, nx_mask);
+            sastage.issue(p.satape, vbase + t_begin(nx) * stride, stride, n_steps(nx), wave, lane);
+        }
         if (nx_load) load_block(state_src(nx), Snext);
+        if (fin_pending) {
+            finalize(fin_buf, fin_tb, fin_nst);
+            fin_pending = false;
+        }
         const float *L = &stg[buf][0][0][0];
-        float *Lsa = &stg[buf][kSA][0][0];
         const int nst = n_steps(it);
         const int64_t tb = t_begin(it);
 
@@ -324,8 +368,7 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
 #pragma unroll
             for (int j = 0; j < KS; ++j) {
                 if (j + 1 < KS) load_fwd(L + (j + 1) * N, fv[(j + 1) & 1]);
-                float sa[R];
-                fwd_step(fv[j & 1], S, sa);
+                fwd_step(fv[j & 1], S);
             }
             if (it.s + 1 <= nsub_of(it.c) - 2)
                 store_block(p.sub + (bh * p.nsubw + it.s) * NN, S);
@@ -347,9 +390,7 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
                     for (int e = 0; e < R; ++e)
 #pragma unroll
                         for (int c = 0; c < CC; ++c) P[j + 1][e][c] = P[j][e][c];
-                    float sa[R];
-                    fwd_step(fv[j & 1], P[j + 1], sa);
-                    row_store(Lsa + j * N, sa);
+                    fwd_step(fv[j & 1], P[j + 1]);
                 }
                 // ... then run the KS reverse steps on them
                 RevVals rv[2];
@@ -357,7 +398,7 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
 #pragma unroll
                 for (int j = KS - 1; j >= 0; --j) {
                     if (j > 0) load_rev(L + (j - 1) * N, rv[(j - 1) & 1]);
-                    rev_step(j, rv[j & 1], P[j], P[j + 1]);
+                    rev_step(j, pb, rv[j & 1], P[j], P[j + 1]);
                 }
             } else {
                 // tail of the sequence: fewer than KS steps
@@ -370,9 +411,7 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
                         for (int e = 0; e < R; ++e)
 #pragma unroll
                             for (int c = 0; c < CC; ++c) P[j + 1][e][c] = P[j][e][c];
-                        float sa[R];
-                        fwd_step(fv, P[j + 1], sa);
-                        row_store(Lsa + j * N, sa);
+                        fwd_step(fv, P[j + 1]);
                     }
                 }
 #pragma unroll
@@ -380,38 +419,20 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
                     if (j < nst) {
                         RevVals rv;
                         load_rev(L + j * N, rv);
-                        rev_step(j, rv, P[j], P[j + 1]);
+                        rev_step(j, pb, rv, P[j], P[j + 1]);
                     }
                 }
             }
-            __syncthreads();
-            // ---- outputs of the sub-chunk: the column sums (fixed-order sum
-            // over waves) and dv, written row-contiguous per step
-            for (int idx = tid; idx < nst * (NQ + 1) * N; idx += NT) {
-                const int col = idx % N;
-                const int q = (idx / N) % (NQ + 1);
-                const int j = idx / (N * (NQ + 1));
-                float xo;
-                float *dst;
-                if (q == NQ) {
-                    xo = dvb[j][col];
-                    dst = p.dv;
-                } else {
-                    xo = part[j][q][0][col];
-#pragma unroll
-                    for (int w = 1; w < NW; ++w) xo += part[j][q][w][col];
-                    dst = p.dr;
-                    if (q == qDK) dst = p.dk;
-                    if (q == qDB) dst = p.db;
-                    if (q == qDW) dst = p.dw;
-                    if (q == qDA) dst = p.da;
-                }
-                dst[vbase + (tb + j) * stride + col] = xo;
-            }
+            fin_pending = true;
+            fin_buf = pb;
+            fin_tb = tb;
+            fin_nst = nst;
+            pb ^= 1;
         }
 
         if (have_next) {
-            stage.commit(&stg[buf ^ 1][0][0][0], n_steps(nx), wave, lane);
+            stage.commit(&stg[buf ^ 1][0][0][0], n_steps(nx), wave, lane, nx_mask);
+            sastage.commit(&stg[buf ^ 1][kSA][0][0], n_steps(nx), wave, lane);
             if (nx_load) {
 #pragma unroll
                 for (int e = 0; e < R; ++e)
@@ -424,6 +445,7 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
         it = nx;
     }
 
+    if (fin_pending) finalize(fin_buf, fin_tb, fin_nst);
     if (p.ds0) store_block(p.ds0 + bh * NN, G);
 }
 
@@ -433,6 +455,7 @@ hipError_t launch_bwd_t(const BwdLaunch &a, hipStream_t stream)
     BwdArgs<TIn> p;
     for (int i = 0; i < 7; ++i) p.in.p[i] = static_cast<const TIn *>(a.in[i]);
     p.ckpt = a.ckpt;
+    p.satape.p[0] = a.satape;
     p.dsT = a.dsT;
     p.dr = a.grad[0];
     p.dw = a.grad[1];

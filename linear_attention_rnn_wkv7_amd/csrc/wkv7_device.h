@@ -37,15 +37,17 @@ __device__ __forceinline__ float group_allreduce(float x)
 }
 
 // Exchange-and-add across lane bit 5: the result in lanes 0-31 is x summed
-// over lane l and l^32; in lanes 32-63 it is y summed the same way.
-// v_permlane32_swap exchanges the upper half of its first operand with the
-// lower half of its second.  Written as inline asm: this compiler folds the
-// sum of the two results of __builtin_amdgcn_permlane32_swap into twice the
-// first result.  The s_nop 1 pairs keep two wait states around the swap.
+// over lane l and l^32; in lanes 32-63 it is y summed the same way
+// (v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second).  The empty asm keeps the two results distinct:
+// without it this compiler folds their sum into twice the first result.
 __device__ __forceinline__ float swap_add32(float x, float y)
 {
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
-    return x + y;
+    auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                              __builtin_bit_cast(unsigned, y), false, false);
+    unsigned lo = p[0], hi = p[1];
+    asm volatile("" : "+v"(hi));
+    return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
 }
 
 // The same across lane bit 4 (v_permlane16_swap exchanges the odd 16-lane
@@ -53,8 +55,11 @@ __device__ __forceinline__ float swap_add32(float x, float y)
 // bit 4 clear get x summed over l and l^16, lanes with bit 4 set get y.
 __device__ __forceinline__ float swap_add16(float x, float y)
 {
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
-    return x + y;
+    auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x),
+                                              __builtin_bit_cast(unsigned, y), false, false);
+    unsigned lo = p[0], hi = p[1];
+    asm volatile("" : "+v"(hi));
+    return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
@@ -110,7 +115,8 @@ struct Stager {
     // vectors 2s and 2s+1 in the two lane halves (half chunks).  Wave w owns
     // slots w, w + kNW, ...
     __device__ __forceinline__ void issue(const VecPtrs<TIn, NV> &vec, int64_t base_t0,
-                                          int64_t step_stride, int nsteps, int wave, int lane)
+                                          int64_t step_stride, int nsteps, int wave, int lane,
+                                          unsigned mask = ~0u)
     {
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
@@ -120,6 +126,7 @@ struct Stager {
                 if (slot >= kSlots || wave != w) continue;
                 if constexpr (!kHalf) {
                     const int q = slot / kCPV;
+                    if (!((mask >> q) & 1u)) continue;
                     const int unit = (slot % kCPV) * kWave + lane;
                     const int st = unit / (N / 4), n4 = unit % (N / 4);
                     if (st < nsteps)
@@ -130,7 +137,8 @@ struct Stager {
                     const int st = unit / (N / 4), n4 = unit % (N / 4);
                     const TIn *src = vec.p[q0];
                     if (q0 + 1 < NV && lane >= 32) src = vec.p[q0 + 1];
-                    const bool valid = st < nsteps && (q0 + 1 < NV || lane < 32);
+                    const int qh = q0 + (lane >> 5);
+                    const bool valid = st < nsteps && qh < NV && ((mask >> qh) & 1u);
                     if (valid)
                         buf[k] = InQuad<TIn>::load(src + base_t0 + st * step_stride + 4 * n4);
                 }
@@ -138,7 +146,8 @@ struct Stager {
         }
     }
 
-    __device__ __forceinline__ void commit(float *lds, int nsteps, int wave, int lane)
+    __device__ __forceinline__ void commit(float *lds, int nsteps, int wave, int lane,
+                                           unsigned mask = ~0u)
     {
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
@@ -148,6 +157,7 @@ struct Stager {
                 if (slot >= kSlots || wave != w) continue;
                 if constexpr (!kHalf) {
                     const int q = slot / kCPV;
+                    if (!((mask >> q) & 1u)) continue;
                     const int unit = (slot % kCPV) * kWave + lane;
                     const int st = unit / (N / 4);
                     if (st < nsteps)
@@ -157,7 +167,7 @@ struct Stager {
                     const int q = 2 * slot + (lane >> 5);
                     const int unit = lane & 31;
                     const int st = unit / (N / 4);
-                    if (st < nsteps && q < NV)
+                    if (st < nsteps && q < NV && ((mask >> q) & 1u))
                         *reinterpret_cast<float4 *>(lds + 4 * (q * kUnitsPerVec + unit)) =
                             InQuad<TIn>::f32(buf[k]);
                 }

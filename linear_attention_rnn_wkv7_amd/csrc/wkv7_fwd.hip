@@ -41,6 +41,7 @@ struct FwdArgs {
     VecPtrs<TIn, 6> in;
     const float *s0;
     float *y, *sT, *ckpt;
+    float *sa;               // per-step sa = S_{t-1} a_t, [B][T][H][N]; may be null
     int64_t T, H;
     int chunk, nck;
 };
@@ -53,6 +54,10 @@ wkv7_fwd_kernel(FwdArgs<TIn> p)
     constexpr int R = Gm::R, CC = Gm::CC, LPR = Gm::LPR, RW = Gm::RW, NT = Gm::NT;
     constexpr int TB = Gm::TB, NV = Gm::NV;
     __shared__ __align__(16) float lds[2][NV][TB][N];
+    // y and sa of a block, [buffer][0 = y, 1 = sa][step][row], written one
+    // value per lane per step and copied out row-contiguous per block
+    __shared__ __align__(16) float outb[2][2][TB][N];
+    __shared__ float sink[NT];   // target of the lanes that hold no value
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cg = lane % LPR, rg = lane / LPR;
@@ -101,9 +106,19 @@ wkv7_fwd_kernel(FwdArgs<TIn> p)
 #pragma unroll
         for (int e = 0; e < R; ++e) sv.v[e] = Ls[kV * TB * N + row0 + e];
     };
-    // One step on S; returns this lane's rows of y (already summed).
-    auto do_step = [&](const StepVals &sv, float (&yv)[R]) {
-        float sa[R], u[R][CC];
+    // Where this lane parks one value of a per-row output: lanes cg < R hold
+    // row row0 + cg; the others write to a private sink slot (no branch).
+    auto park = [&](float *row_base, const float (&x)[R]) {
+        float val = x[0];
+#pragma unroll
+        for (int e = 1; e < R; ++e)
+            if (cg == e) val = x[e];
+        float *dst = cg < R ? row_base + row0 + cg : &sink[tid];
+        *dst = val;
+    };
+    // One step on S; parks this lane's rows of y and sa in LDS.
+    auto do_step = [&](const StepVals &sv, float *ypark, float *sapark) {
+        float sa[R], u[R][CC], yv[R];
 #pragma unroll
         for (int e = 0; e < R; ++e) {
             // sa = S a over the pre-update state: two partial chains, then
@@ -132,6 +147,8 @@ wkv7_fwd_kernel(FwdArgs<TIn> p)
             }
             yv[e] = group_allreduce<LPR>(y0 + y1);
         }
+        park(ypark, yv);
+        park(sapark, sa);
     };
 
     // Input staging runs two blocks ahead: while block b computes from LDS,
@@ -171,6 +188,24 @@ wkv7_fwd_kernel(FwdArgs<TIn> p)
         }
     };
 
+    // Copy the parked y and sa of block blk (in outb[blk & 1]) to HBM: each
+    // step is N contiguous floats per output.
+    auto copy_out = [&](int64_t blk) {
+        const int64_t t0 = blk * TB;
+        const int nst = steps_of(blk);
+        constexpr int kQ = 2 * TB * N / 4;            // float4 units
+#pragma unroll
+        for (int k = 0; k < (kQ + NT - 1) / NT; ++k) {
+            const int u = tid + k * NT;
+            const int which = u / (TB * N / 4);       // 0 = y, 1 = sa
+            const int st = (u / (N / 4)) % TB, n4 = u % (N / 4);
+            float *base = which == 0 ? p.y : p.sa;
+            if (u < kQ && st < nst && base)
+                *reinterpret_cast<float4 *>(base + vbase + (t0 + st) * stride + 4 * n4) =
+                    *reinterpret_cast<const float4 *>(&outb[blk & 1][which][st][4 * n4]);
+        }
+    };
+
     // One block; `mine` holds this block's registers slot (free now: it was
     // committed before this block) and `other` holds block blk+1.
     auto run_block = [&](int64_t blk, StagerT &mine, StagerT &other) {
@@ -178,9 +213,11 @@ wkv7_fwd_kernel(FwdArgs<TIn> p)
         const int nst = steps_of(blk);
         if (blk + 2 < nblk)
             mine.issue(p.in, vbase + (t0 + 2 * TB) * stride, stride, steps_of(blk + 2), wave, lane);
+        if (blk > 0) copy_out(blk - 1);
 
         const float *L = &lds[blk & 1][0][0][0];
-        float ybuf[TB][R];
+        float *Y = &outb[blk & 1][0][0][0];
+        float *SA = &outb[blk & 1][1][0][0];
         if (nst == TB) {
             // steady state: straight-line code except the rare mid-block
             // checkpoint test; the next step's operands are read from LDS
@@ -191,7 +228,7 @@ wkv7_fwd_kernel(FwdArgs<TIn> p)
             for (int s = 0; s < TB; ++s) {
                 if (s == 0 || s == 8) maybe_checkpoint(t0 + s);
                 if (s + 1 < TB) load_step(L + (s + 1) * N, sv[(s + 1) & 1]);
-                do_step(sv[s & 1], ybuf[s]);
+                do_step(sv[s & 1], Y + s * N, SA + s * N);
             }
         } else {
 #pragma unroll
@@ -200,34 +237,10 @@ wkv7_fwd_kernel(FwdArgs<TIn> p)
                     if (s == 0 || s == 8) maybe_checkpoint(t0 + s);
                     StepVals sv;
                     load_step(L + s * N, sv);
-                    do_step(sv, ybuf[s]);
+                    do_step(sv, Y + s * N, SA + s * N);
                 }
             }
         }
-        // y of the block: lane cg of each row group writes step cg (+LPR...).
-        if (p.y) {
-#pragma unroll
-            for (int s0 = 0; s0 < TB; s0 += LPR) {
-                const int s = s0 + cg;
-                float yo[R];
-#pragma unroll
-                for (int e = 0; e < R; ++e) {
-                    yo[e] = ybuf[s0][e];
-#pragma unroll
-                    for (int q = 1; q < LPR && s0 + q < TB; ++q)
-                        if (cg == q) yo[e] = ybuf[s0 + q][e];
-                }
-                if (s < nst) {
-                    float *dst = p.y + vbase + (t0 + s) * stride + row0;
-                    if constexpr (R == 2)
-                        *reinterpret_cast<float2 *>(dst) = make_float2(yo[0], yo[1]);
-                    else
-#pragma unroll
-                        for (int e = 0; e < R; ++e) dst[e] = yo[e];
-                }
-            }
-        }
-
         if (blk + 1 < nblk)
             other.commit(&lds[(blk + 1) & 1][0][0][0], steps_of(blk + 1), wave, lane);
         __syncthreads();
@@ -238,6 +251,7 @@ wkv7_fwd_kernel(FwdArgs<TIn> p)
         else
             run_block(blk, stage1, stage0);
     }
+    if (nblk > 0) copy_out(nblk - 1);
 
     if (p.sT) {
         float *dst = p.sT + bh * N * N + (int64_t)row0 * N + col0;
@@ -259,6 +273,7 @@ hipError_t launch_fwd_t(const FwdLaunch &a, hipStream_t stream)
     p.y = a.y;
     p.sT = a.sT;
     p.ckpt = a.ckpt;
+    p.sa = a.satape;
     p.T = a.T;
     p.H = a.H;
     p.chunk = a.chunk;

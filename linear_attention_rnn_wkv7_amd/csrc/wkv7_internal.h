@@ -15,6 +15,7 @@ struct FwdLaunch {
     const void *in[6];       // r, w, k, v, a, b
     const float *s0;         // may be null (zeros)
     float *y, *sT, *ckpt;    // each may be null (skipped)
+    float *satape;           // per-step sa, [B][T][H][N]; may be null
     int64_t B, T, H, N;
     int dtype;               // 0 f32, 1 bf16
     int chunk;               // checkpoint interval
@@ -23,6 +24,7 @@ struct FwdLaunch {
 struct BwdLaunch {
     const void *in[7];       // r, w, k, v, a, b, dy
     const float *ckpt;       // required
+    const float *satape;     // required: the forward's per-step sa
     const float *dsT;        // may be null (zeros)
     float *grad[6];          // dr, dw, dk, dv, da, db
     float *ds0;              // may be null

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.wkv7_abi_version() == 100
+    assert L.wkv7_abi_version() == 101
 
 
 def _shape(B=2, T=10, H=3, N=64, dtype=0, chunk=64):
@@ -102,13 +102,15 @@ def test_backward_validation():
 def test_size_queries():
     L = _lib.lib()
     sh = _shape(B=8, T=4096, H=32, N=64)
-    assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == 8 * 32 * 64 * 64 * 64 * 4
+    # states every 64 steps, then the per-step sa tape
+    ck = 8 * 32 * 64 * 64 * 64 * 4 + 8 * 4096 * 32 * 64 * 4
+    assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == ck
     # 7 sub-checkpoint slots of one chunk per (b, h)
     assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) == 8 * 32 * 7 * 64 * 64 * 4
-    ck = 8 * 32 * 64 * 64 * 64 * 4
     assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 0) == 8 * 32 * 7 * 64 * 64 * 4 + ck
     sh = _shape(B=1, T=65, H=1, N=16, chunk=8)
-    assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == 9 * 16 * 16 * 4
+    # 9 states of 1 KiB (rounded up to 256 B) + 65 steps of sa
+    assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == 9 * 16 * 16 * 4 + 65 * 16 * 4
     assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) == 0
     assert L.wkv7_checkpoint_bytes(ctypes.byref(_shape(N=48))) == 0
     assert L.wkv7_checkpoint_bytes(None) == 0
