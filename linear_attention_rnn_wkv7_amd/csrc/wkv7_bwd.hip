@@ -327,17 +327,20 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
     // also needs r, a, dy
     constexpr unsigned kMaskA = (1u << kW) | (1u << kK) | (1u << kV) | (1u << kB);
     constexpr unsigned kMaskB = (1u << NV) - 1u;
-    Stager<TIn, NV, KS, N, NT> stage;
-    Stager<float, 1, KS, N, NT> sastage;
+    using StagerT = InputStager<TIn, NV, KS, N, NT>;
+    StagerT stage;                          // inputs: DMA for fp32, registers for bf16
+    DmaStager<1, KS, N, NT> sastage;        // the fp32 sa tape
     float S[R][CC], Snext[R][CC];
     Item it = first_of(p.nck - 1);
     {
         const unsigned m = it.B ? kMaskB : kMaskA;
-        stage.issue(p.in, vbase + t_begin(it) * stride, stride, n_steps(it), wave, lane, m);
-        sastage.issue(p.satape, vbase + t_begin(it) * stride, stride, n_steps(it), wave, lane);
+        stage.issue(p.in, vbase + t_begin(it) * stride, stride, n_steps(it), wave, lane,
+                    &stg[0][0][0][0], m);
+        sastage.issue(p.satape, vbase + t_begin(it) * stride, stride, n_steps(it), wave, lane,
+                      &stg[0][kSA][0][0]);
         load_block(state_src(it), S);
         stage.commit(&stg[0][0][0][0], n_steps(it), wave, lane, m);
-        sastage.commit(&stg[0][kSA][0][0], n_steps(it), wave, lane);
+        wait_dma();
     }
     __syncthreads();
     int buf = 0;
@@ -348,8 +351,10 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
         const bool nx_load = have_next && loads_state(nx);
         const unsigned nx_mask = nx.B ? kMaskB : kMaskA;
         if (have_next) {
-            stage.issue(p.in, vbase + t_begin(nx) * stride, stride, n_steps(nx), wave, lane, nx_mask);
-            sastage.issue(p.satape, vbase + t_begin(nx) * stride, stride, n_steps(nx), wave, lane);
+            stage.issue(p.in, vbase + t_begin(nx) * stride, stride, n_steps(nx), wave, lane,
+                        &stg[buf ^ 1][0][0][0], nx_mask);
+            sastage.issue(p.satape, vbase + t_begin(nx) * stride, stride, n_steps(nx), wave, lane,
+                          &stg[buf ^ 1][kSA][0][0]);
         }
         if (nx_load) load_block(state_src(nx), Snext);
         if (fin_pending) {
@@ -432,7 +437,6 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
 
         if (have_next) {
             stage.commit(&stg[buf ^ 1][0][0][0], n_steps(nx), wave, lane, nx_mask);
-            sastage.commit(&stg[buf ^ 1][kSA][0][0], n_steps(nx), wave, lane);
             if (nx_load) {
 #pragma unroll
                 for (int e = 0; e < R; ++e)
@@ -440,6 +444,7 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
                     for (int c = 0; c < CC; ++c) S[e][c] = Snext[e][c];
             }
         }
+        wait_dma();
         __syncthreads();
         buf ^= 1;
         it = nx;

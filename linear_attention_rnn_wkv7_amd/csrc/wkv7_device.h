@@ -176,4 +176,96 @@ struct Stager {
     }
 };
 
+// Direct HBM -> LDS staging (gfx950 global_load_lds_dwordx4) for fp32
+// inputs: the same chunk ownership and LDS layout as Stager, but each wave
+// instruction writes its 64 lanes' float4s straight into 1 KB of LDS, so no
+// registers hold the block in flight.  The copies are complete after
+// `s_waitcnt vmcnt(0)` (wait_dma) in the issuing wave; a barrier after that
+// publishes them to the workgroup.
+__device__ __forceinline__ void wait_dma()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// One lane's 16 bytes from global memory to LDS at lds_wave_base + lane * 16
+// (the wave-uniform LDS byte address goes through M0).  Written as inline
+// asm so the compiler does not treat later LDS reads as possibly reading
+// this copy: it would otherwise wait for every copy in flight before each
+// LDS read.  Completion is awaited explicitly with wait_dma().
+__device__ __forceinline__ void dma16(const void *gsrc, const float *lds_wave_base)
+{
+    const unsigned m0 = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) float *)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gsrc), "s"(m0)
+                 : "memory", "m0");
+}
+
+template <int NV, int TB, int N, int NTHREADS>
+struct DmaStager {
+    using Geo = Stager<float, NV, TB, N, NTHREADS>;
+    static constexpr int kNW = Geo::kNW, kUnitsPerVec = Geo::kUnitsPerVec, kCPV = Geo::kCPV;
+    static constexpr bool kHalf = Geo::kHalf;
+    static constexpr int kSlots = Geo::kSlots, kPer = Geo::kPer;
+
+    __device__ __forceinline__ void issue(const VecPtrs<float, NV> &vec, int64_t base_t0,
+                                          int64_t step_stride, int nsteps, int wave, int lane,
+                                          float *lds, unsigned mask = ~0u)
+    {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+#pragma unroll
+            for (int w = 0; w < kNW; ++w) {
+                const int slot = k * kNW + w;
+                if (slot >= kSlots || wave != w) continue;
+                if constexpr (!kHalf) {
+                    const int q = slot / kCPV;
+                    if (!((mask >> q) & 1u)) continue;
+                    const int chunk = slot % kCPV;
+                    const int unit = chunk * kWave + lane;
+                    const int st = unit / (N / 4), n4 = unit % (N / 4);
+                    if (st < nsteps)
+                        dma16(vec.p[q] + base_t0 + st * step_stride + 4 * n4,
+                              lds + 4 * (q * kUnitsPerVec + chunk * kWave));
+                } else {
+                    // lanes 0-31 carry vector 2*slot, lanes 32-63 the next one,
+                    // which follows it in LDS
+                    const int q0 = 2 * slot;
+                    const int qh = q0 + (lane >> 5);
+                    const int unit = lane & 31;
+                    const int st = unit / (N / 4), n4 = unit % (N / 4);
+                    const float *src = vec.p[q0];
+                    if (q0 + 1 < NV && lane >= 32) src = vec.p[q0 + 1];
+                    if (st < nsteps && qh < NV && ((mask >> qh) & 1u))
+                        dma16(src + base_t0 + st * step_stride + 4 * n4,
+                              lds + 4 * (q0 * kUnitsPerVec));
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void commit(float *, int, int, int, unsigned = ~0u) {}
+};
+
+// The input stager for a dtype: DMA for fp32, registers (widening) for bf16.
+template <typename TIn, int NV, int TB, int N, int NTHREADS>
+struct InputStager {
+    Stager<TIn, NV, TB, N, NTHREADS> st;
+    static constexpr bool kDma = false;
+    __device__ __forceinline__ void issue(const VecPtrs<TIn, NV> &vec, int64_t base_t0,
+                                          int64_t step_stride, int nsteps, int wave, int lane,
+                                          float *, unsigned mask = ~0u)
+    {
+        st.issue(vec, base_t0, step_stride, nsteps, wave, lane, mask);
+    }
+    __device__ __forceinline__ void commit(float *lds, int nsteps, int wave, int lane,
+                                           unsigned mask = ~0u)
+    {
+        st.commit(lds, nsteps, wave, lane, mask);
+    }
+};
+template <int NV, int TB, int N, int NTHREADS>
+struct InputStager<float, NV, TB, N, NTHREADS> : DmaStager<NV, TB, N, NTHREADS> {
+    static constexpr bool kDma = true;
+};
+
 }  // namespace wkv7

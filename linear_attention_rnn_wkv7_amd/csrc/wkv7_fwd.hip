@@ -29,7 +29,7 @@ struct FwdGeom {
     static constexpr int RW = (kWave / LPR) * R;    // rows per wave
     static constexpr int NW = N / RW;               // waves per workgroup
     static constexpr int NT = NW * kWave;
-    static constexpr int TB = 16;                   // steps per staged block
+    static constexpr int TB = 32;                   // steps per staged block
     static constexpr int NV = 6;                    // r, w, k, v, a, b
     static_assert(N % RW == 0 && CC % 4 == 0, "tile");
 };
@@ -151,26 +151,26 @@ wkv7_fwd_kernel(FwdArgs<TIn> p)
         park(sapark, sa);
     };
 
-    // Input staging runs two blocks ahead: while block b computes from LDS,
-    // block b+1 sits in registers (loaded during block b-1) and block b+2 is
-    // being loaded.  stage[x & 1] holds block x.
-    using StagerT = Stager<TIn, NV, TB, N, NT>;
-    StagerT stage0, stage1;
+    // Input staging runs one block ahead: while block b computes from
+    // lds[b & 1], block b+1 is copied into lds[(b+1) & 1] (directly from HBM
+    // for fp32 inputs, through registers for bf16).
+    using StagerT = InputStager<TIn, NV, TB, N, NT>;
+    StagerT stage;
     const int64_t nblk = (T + TB - 1) / TB;
     auto steps_of = [&](int64_t blk) -> int {
         const int64_t rem = T - blk * TB;
         return (int)(rem < TB ? rem : TB);
     };
     if (nblk > 0) {
-        stage0.issue(p.in, vbase, stride, steps_of(0), wave, lane);
-        if (nblk > 1) stage1.issue(p.in, vbase + TB * stride, stride, steps_of(1), wave, lane);
-        stage0.commit(&lds[0][0][0][0], steps_of(0), wave, lane);
+        stage.issue(p.in, vbase, stride, steps_of(0), wave, lane, &lds[0][0][0][0]);
+        stage.commit(&lds[0][0][0][0], steps_of(0), wave, lane);
+        if constexpr (StagerT::kDma) wait_dma();
     }
     __syncthreads();
 
     // Checkpoints: the state before every step that is a multiple of the
-    // chunk (a multiple of 8, so within a block only offsets 0 and 8).
-    static_assert(TB == 16, "checkpoint offsets assume 16-step blocks");
+    // chunk (a multiple of 8, so within a block only offsets 0, 8, 16, ...).
+    static_assert(TB % 8 == 0, "checkpoint offsets are multiples of 8");
     int64_t next_ck = 0, ck_slot = 0;
     auto maybe_checkpoint = [&](int64_t t) {
         if (t == next_ck) {
@@ -206,13 +206,12 @@ wkv7_fwd_kernel(FwdArgs<TIn> p)
         }
     };
 
-    // One block; `mine` holds this block's registers slot (free now: it was
-    // committed before this block) and `other` holds block blk+1.
-    auto run_block = [&](int64_t blk, StagerT &mine, StagerT &other) {
+    for (int64_t blk = 0; blk < nblk; ++blk) {
         const int64_t t0 = blk * TB;
         const int nst = steps_of(blk);
-        if (blk + 2 < nblk)
-            mine.issue(p.in, vbase + (t0 + 2 * TB) * stride, stride, steps_of(blk + 2), wave, lane);
+        if (blk + 1 < nblk)
+            stage.issue(p.in, vbase + (t0 + TB) * stride, stride, steps_of(blk + 1), wave, lane,
+                        &lds[(blk + 1) & 1][0][0][0]);
         if (blk > 0) copy_out(blk - 1);
 
         const float *L = &lds[blk & 1][0][0][0];
@@ -226,7 +225,7 @@ wkv7_fwd_kernel(FwdArgs<TIn> p)
             load_step(L, sv[0]);
 #pragma unroll
             for (int s = 0; s < TB; ++s) {
-                if (s == 0 || s == 8) maybe_checkpoint(t0 + s);
+                if (s % 8 == 0) maybe_checkpoint(t0 + s);
                 if (s + 1 < TB) load_step(L + (s + 1) * N, sv[(s + 1) & 1]);
                 do_step(sv[s & 1], Y + s * N, SA + s * N);
             }
@@ -234,22 +233,16 @@ wkv7_fwd_kernel(FwdArgs<TIn> p)
 #pragma unroll
             for (int s = 0; s < TB; ++s) {
                 if (s < nst) {
-                    if (s == 0 || s == 8) maybe_checkpoint(t0 + s);
+                    if (s % 8 == 0) maybe_checkpoint(t0 + s);
                     StepVals sv;
                     load_step(L + s * N, sv);
                     do_step(sv, Y + s * N, SA + s * N);
                 }
             }
         }
-        if (blk + 1 < nblk)
-            other.commit(&lds[(blk + 1) & 1][0][0][0], steps_of(blk + 1), wave, lane);
+        if (blk + 1 < nblk) stage.commit(&lds[(blk + 1) & 1][0][0][0], steps_of(blk + 1), wave, lane);
+        if constexpr (StagerT::kDma) wait_dma();
         __syncthreads();
-    };
-    for (int64_t blk = 0; blk < nblk; ++blk) {
-        if ((blk & 1) == 0)
-            run_block(blk, stage0, stage1);
-        else
-            run_block(blk, stage1, stage0);
     }
     if (nblk > 0) copy_out(nblk - 1);
 
