@@ -60,6 +60,25 @@ typedef enum {
     WKV7_BF16 = 1
 } wkv7_dtype;
 
+/* How wkv7_backward computes the gradients (the results agree to rounding).
+ *   AUTO    : the chunk form where it applies (N = 64 and C = 64), the step
+ *             scan elsewhere.
+ *   SCAN    : the step-by-step reverse scan: regenerate the states of a
+ *             chunk from its checkpoint, then run the reverse recurrence.
+ *   CHUNKED : the chunk form (WKV7_ERR_UNSUPPORTED where it does not apply).
+ *             Per 64-step chunk it runs only dsa = G b step by step and forms
+ *             every gradient from dense products of the chunk's vectors with
+ *             the checkpointed state and the incoming state gradient.  It
+ *             takes decays w in [1/16, 1] whose product over a chunk stays
+ *             above 2^-60; for a head whose inputs leave that range it falls
+ *             back to SCAN for that head by itself.
+ * The forward ignores this field. */
+typedef enum {
+    WKV7_ALGO_AUTO = 0,
+    WKV7_ALGO_SCAN = 1,
+    WKV7_ALGO_CHUNKED = 2
+} wkv7_algo;
+
 typedef struct {
     int64_t B;      /* batch, >= 0 */
     int64_t T;      /* time steps, >= 0 */
@@ -68,13 +87,16 @@ typedef struct {
     int32_t dtype;  /* wkv7_dtype */
     int32_t chunk;  /* checkpoint interval C: 0 means 64; else a multiple of
                        8 in [8, 4096] */
+    int32_t algo;   /* wkv7_algo (backward only) */
+    int32_t reserved; /* must be 0 */
 } wkv7_shape;
 
 enum {
     WKV7_OK = 0,
     WKV7_ERR_INVALID = -1,      /* NULL/misaligned pointer, negative size,
-                                   bad dtype or chunk, size overflow */
-    WKV7_ERR_UNSUPPORTED = -2,  /* N not in {16, 64} */
+                                   bad dtype, chunk or algo, size overflow */
+    WKV7_ERR_UNSUPPORTED = -2,  /* N not in {16, 64}; CHUNKED where it does
+                                   not apply */
     WKV7_ERR_WORKSPACE = -3,    /* workspace missing or too small */
     WKV7_ERR_HIP = -4           /* a kernel launch failed */
 };
@@ -84,8 +106,9 @@ enum {
 size_t wkv7_checkpoint_bytes(const wkv7_shape *shape);
 
 /* Bytes of device workspace wkv7_backward needs: the per-(b,h) state
- * sub-checkpoints of one chunk, plus room for the checkpoint record itself
- * when `ckpt_provided` is 0.  0 when the shape is invalid or empty. */
+ * sub-checkpoints of one chunk and one int per (b,h), plus room for the
+ * checkpoint record itself when `ckpt_provided` is 0.  0 when the shape is
+ * invalid or empty. */
 size_t wkv7_backward_workspace_bytes(const wkv7_shape *shape, int ckpt_provided);
 
 /* Forward scan (rx_wkv7_forward_seq on the Foundry rx_pretrain.c page).

@@ -10,6 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("WKV7_LIB") or os.path.join(PKG, "libwkv7.so")
 
 WKV7_F32, WKV7_BF16 = 0, 1
+WKV7_ALGO_AUTO, WKV7_ALGO_SCAN, WKV7_ALGO_CHUNKED = 0, 1, 2
 WKV7_OK, WKV7_ERR_INVALID, WKV7_ERR_UNSUPPORTED, WKV7_ERR_WORKSPACE, WKV7_ERR_HIP = 0, -1, -2, -3, -4
 
 # Every function the C header declares, for the symbol-export test.
@@ -19,7 +20,8 @@ EXPORTS = ("wkv7_checkpoint_bytes", "wkv7_backward_workspace_bytes", "wkv7_forwa
 
 class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
-                ("N", ctypes.c_int64), ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32)]
+                ("N", ctypes.c_int64), ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("algo", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class Wkv7Error(RuntimeError):

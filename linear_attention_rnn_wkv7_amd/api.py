@@ -22,8 +22,12 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def make_shape(B, T, H, N, dtype=torch.float32, chunk=64):
-    return _lib.Shape(B, T, H, N, _VEC_DTYPES[dtype], chunk)
+_ALGOS = {"auto": _lib.WKV7_ALGO_AUTO, "scan": _lib.WKV7_ALGO_SCAN,
+          "chunked": _lib.WKV7_ALGO_CHUNKED}
+
+
+def make_shape(B, T, H, N, dtype=torch.float32, chunk=64, algo="auto"):
+    return _lib.Shape(B, T, H, N, _VEC_DTYPES[dtype], chunk, _ALGOS[algo], 0)
 
 
 def _check_vecs(names, tensors):
@@ -87,8 +91,10 @@ def wkv7_forward(r, w, k, v, a, b, s0=None, *, chunk=64, want_y=True, want_sT=Tr
 
 
 def wkv7_backward(r, w, k, v, a, b, dy, s0=None, dsT=None, ckpt=None, *, chunk=64,
-                  want_ds0=True, workspace=None, stream=None, out=None):
-    """Run the reverse scan.  Returns dict(dr, dw, dk, dv, da, db, ds0)."""
+                  want_ds0=True, workspace=None, stream=None, out=None, algo="auto"):
+    """Run the reverse scan.  Returns dict(dr, dw, dk, dv, da, db, ds0).
+
+    algo: "auto", "scan" or "chunked" (wkv7_algo)."""
     (B, T, H, N), dt = _check_vecs("rwkvab dy", (r, w, k, v, a, b, dy))
     _check_state("s0", s0, B, H, N)
     _check_state("dsT", dsT, B, H, N)
@@ -106,7 +112,7 @@ def wkv7_backward(r, w, k, v, a, b, dy, s0=None, dsT=None, ckpt=None, *, chunk=6
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    sh = make_shape(B, T, H, N, dt, chunk)
+    sh = make_shape(B, T, H, N, dt, chunk, algo)
     rc = _lib.lib().wkv7_backward(
         ctypes.byref(sh), *map(_ptr, (r, w, k, v, a, b, s0, dy, dsT, ckpt)),
         *map(_ptr, (grads[n] for n in names)), _ptr(grads["ds0"]),

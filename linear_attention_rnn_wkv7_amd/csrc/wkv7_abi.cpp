@@ -13,7 +13,7 @@ constexpr size_t kAlign = 256;   // workspace sub-buffer alignment
 
 struct Dims {
     int64_t B, T, H, N, C, nck;
-    int dtype;
+    int dtype, algo;
     size_t vec_elems, state_elems;   // per tensor
 };
 
@@ -27,6 +27,8 @@ int check_shape(const wkv7_shape *s, Dims *d)
     if (!s) return WKV7_ERR_INVALID;
     if (s->B < 0 || s->T < 0 || s->H < 0 || s->N <= 0) return WKV7_ERR_INVALID;
     if (s->dtype != WKV7_F32 && s->dtype != WKV7_BF16) return WKV7_ERR_INVALID;
+    if (s->algo < WKV7_ALGO_AUTO || s->algo > WKV7_ALGO_CHUNKED || s->reserved != 0)
+        return WKV7_ERR_INVALID;
     const int64_t C = s->chunk == 0 ? 64 : s->chunk;
     if (C < 8 || C > 4096 || C % 8 != 0) return WKV7_ERR_INVALID;
     if (s->N != 16 && s->N != 64) return WKV7_ERR_UNSUPPORTED;
@@ -45,6 +47,7 @@ int check_shape(const wkv7_shape *s, Dims *d)
     d->C = C;
     d->nck = nck;
     d->dtype = s->dtype;
+    d->algo = s->algo;
     d->vec_elems = (size_t)vec;
     d->state_elems = (size_t)st;
     return WKV7_OK;
@@ -78,10 +81,21 @@ const float *tape_of(const float *ck, const Dims &d)
                                            round_up(ckpt_state_bytes(d)));
 }
 
-// Sub-checkpoint scratch first, then (when needed) the checkpoints.
+// Sub-checkpoint scratch first, then the per-head flags of the chunk form,
+// then (when needed) the checkpoints.
+size_t sub_region(const Dims &d)
+{
+    return round_up(wkv7::sub_bytes(d.B, d.H, d.N, (int)d.C));
+}
+
+size_t flag_region(const Dims &d)
+{
+    return round_up((size_t)(d.B * d.H) * sizeof(int));
+}
+
 size_t workspace_bytes(const Dims &d, bool ckpt_provided)
 {
-    size_t n = round_up(wkv7::sub_bytes(d.B, d.H, d.N, (int)d.C));
+    size_t n = sub_region(d) + flag_region(d);
     if (!ckpt_provided) n += round_up(ckpt_bytes(d));
     return n;
 }
@@ -170,6 +184,7 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
                           (const void *)ds0})
         if (!aligned(p)) return WKV7_ERR_INVALID;
 
+    if (d.algo == WKV7_ALGO_CHUNKED && !(d.N == 64 && d.C == 64)) return WKV7_ERR_UNSUPPORTED;
     if (d.T == 0) {
         if (!ds0) return WKV7_OK;
         return hip_status(wkv7::launch_fill(ds0, dsT, d.state_elems, stream));
@@ -182,8 +197,7 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
     float *sub = reinterpret_cast<float *>(ws);
     const float *ck = ckpt;
     if (!ckpt) {
-        float *own = reinterpret_cast<float *>(
-            ws + round_up(wkv7::sub_bytes(d.B, d.H, d.N, (int)d.C)));
+        float *own = reinterpret_cast<float *>(ws + sub_region(d) + flag_region(d));
         wkv7::FwdLaunch F;
         for (int i = 0; i < 6; ++i) F.in[i] = in[i];
         F.s0 = s0;
@@ -209,12 +223,14 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
     for (int i = 0; i < 6; ++i) L.grad[i] = grad[i];
     L.ds0 = ds0;
     L.sub = sub;
+    L.flags = reinterpret_cast<int *>(ws + sub_region(d));
     L.B = d.B;
     L.T = d.T;
     L.H = d.H;
     L.N = d.N;
     L.dtype = d.dtype;
     L.chunk = (int)d.C;
+    L.algo = d.algo;
     return hip_status(wkv7::launch_backward(L, stream));
 }
 
@@ -232,7 +248,7 @@ const char *wkv7_status_string(int status)
 
 int wkv7_abi_version(void)
 {
-    return 101;
+    return 102;
 }
 
 }  // extern "C"

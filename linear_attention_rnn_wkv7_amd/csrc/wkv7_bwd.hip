@@ -58,6 +58,7 @@ struct BwdArgs {
     const float *ckpt, *dsT;
     float *dr, *dw, *dk, *dv, *da, *db, *ds0;
     float *sub;
+    const int *only;         // if set, only heads with only[bh] != 0 run
     int64_t T, H;
     int chunk, nck, nsubw;   // nsubw: sub-checkpoint slots per (b, h)
 };
@@ -89,6 +90,7 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
     const int cg = lane % LPR, rg = lane / LPR;
     const int row0 = wave * RW + rg * R, col0 = cg * CC;
     const int64_t bh = blockIdx.x, T = p.T, H = p.H;
+    if (p.only && p.only[bh] == 0) return;   // uniform over the workgroup
     const int64_t b = bh / H, h = bh % H;
     const int64_t stride = H * N;
     const int64_t vbase = (b * T * H + h) * N;
@@ -455,7 +457,7 @@ wkv7_bwd_kernel(BwdArgs<TIn> p)
 }
 
 template <int N, typename TIn>
-hipError_t launch_bwd_t(const BwdLaunch &a, hipStream_t stream)
+hipError_t launch_bwd_t(const BwdLaunch &a, const int *only, hipStream_t stream)
 {
     BwdArgs<TIn> p;
     for (int i = 0; i < 7; ++i) p.in.p[i] = static_cast<const TIn *>(a.in[i]);
@@ -470,6 +472,7 @@ hipError_t launch_bwd_t(const BwdLaunch &a, hipStream_t stream)
     p.db = a.grad[5];
     p.ds0 = a.ds0;
     p.sub = a.sub;
+    p.only = only;
     p.T = a.T;
     p.H = a.H;
     p.chunk = a.chunk;
@@ -497,11 +500,17 @@ size_t sub_bytes(int64_t B, int64_t H, int64_t N, int chunk)
 
 hipError_t launch_backward(const BwdLaunch &a, hipStream_t stream)
 {
+    const int *only = nullptr;
+    if (a.algo != 1 && chunked_backward_supported(a)) {
+        const hipError_t e = launch_backward_chunked(a, a.flags, stream);
+        if (e != hipSuccess) return e;
+        only = a.flags;
+    }
     if (a.N == 64)
-        return a.dtype == 0 ? launch_bwd_t<64, float>(a, stream)
-                            : launch_bwd_t<64, uint16_t>(a, stream);
-    return a.dtype == 0 ? launch_bwd_t<16, float>(a, stream)
-                        : launch_bwd_t<16, uint16_t>(a, stream);
+        return a.dtype == 0 ? launch_bwd_t<64, float>(a, only, stream)
+                            : launch_bwd_t<64, uint16_t>(a, only, stream);
+    return a.dtype == 0 ? launch_bwd_t<16, float>(a, only, stream)
+                        : launch_bwd_t<16, uint16_t>(a, only, stream);
 }
 
 hipError_t launch_fill(float *dst, const float *src, size_t n, hipStream_t stream)

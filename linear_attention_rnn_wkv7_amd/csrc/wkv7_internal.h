@@ -29,16 +29,24 @@ struct BwdLaunch {
     float *grad[6];          // dr, dw, dk, dv, da, db
     float *ds0;              // may be null
     float *sub;              // sub-checkpoint scratch (see sub_bytes)
+    int *flags;              // B*H ints: heads the chunk form could not take
     int64_t B, T, H, N;
     int dtype;
     int chunk;
+    int algo;                // wkv7_algo
 };
 
 // Bytes of sub-checkpoint scratch the backward needs for a shape.
 size_t sub_bytes(int64_t B, int64_t H, int64_t N, int chunk);
 
 hipError_t launch_forward(const FwdLaunch &a, hipStream_t stream);
+// Reverse scan: the chunk form where it applies (and algo allows), then the
+// step-by-step scan for every head the chunk form flagged (or all heads).
 hipError_t launch_backward(const BwdLaunch &a, hipStream_t stream);
+// The chunk form (wkv7_bwdc.hip): N = 64, C = 64.  Writes flags[bh] = 1 for
+// heads whose decays it cannot take (their outputs are then undefined).
+bool chunked_backward_supported(const BwdLaunch &a);
+hipError_t launch_backward_chunked(const BwdLaunch &a, int *flags, hipStream_t stream);
 // dst[i] = src ? src[i] : 0 for i < n.
 hipError_t launch_fill(float *dst, const float *src, size_t n, hipStream_t stream);
 

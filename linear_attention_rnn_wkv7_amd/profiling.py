@@ -18,6 +18,7 @@ import statistics
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ("linear_attention_rnn_wkv7_amd/csrc/wkv7_bwd.hip",
+                  "linear_attention_rnn_wkv7_amd/csrc/wkv7_bwdc.hip",
                   "linear_attention_rnn_wkv7_amd/csrc/wkv7_fwd.hip",
                   "linear_attention_rnn_wkv7_amd/csrc/wkv7_device.h")
 

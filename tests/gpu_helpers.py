@@ -15,13 +15,13 @@ GRADS = ("dr", "dw", "dk", "dv", "da", "db")
 TAU = {torch.float32: 2e-4, torch.bfloat16: 2e-2}
 
 
-def gpu_run(inp, chunk=64, ckpt_handoff=True):
+def gpu_run(inp, chunk=64, ckpt_handoff=True, algo="auto"):
     """Forward (with checkpoints) + backward on the device.  Returns dict of
     fp32 device tensors y, sT, dr..db, ds0."""
     y, sT, ck = api.wkv7_forward(*(inp[n] for n in IN), inp["s0"], chunk=chunk,
                                  want_ckpt=ckpt_handoff)
     g = api.wkv7_backward(*(inp[n] for n in IN), inp["dy"], inp["s0"], inp["dsT"],
-                          ck if ckpt_handoff else None, chunk=chunk)
+                          ck if ckpt_handoff else None, chunk=chunk, algo=algo)
     out = dict(g)
     out["y"], out["sT"] = y, sT
     return out

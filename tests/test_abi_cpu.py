@@ -26,11 +26,11 @@ def test_exports_every_declared_symbol():
     assert declared == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.wkv7_abi_version() == 101
+    assert L.wkv7_abi_version() == 102
 
 
-def _shape(B=2, T=10, H=3, N=64, dtype=0, chunk=64):
-    return _lib.Shape(B, T, H, N, dtype, chunk)
+def _shape(B=2, T=10, H=3, N=64, dtype=0, chunk=64, algo=0, reserved=0):
+    return _lib.Shape(B, T, H, N, dtype, chunk, algo, reserved)
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
@@ -88,6 +88,13 @@ def test_backward_validation():
     for i in range(17):
         assert _bwd(sh, misalign_at=i) == _lib.WKV7_ERR_INVALID, i
     assert _bwd(_shape(N=16, dtype=5)) == _lib.WKV7_ERR_INVALID
+    assert _bwd(_shape(algo=3)) == _lib.WKV7_ERR_INVALID
+    assert _bwd(_shape(algo=-1)) == _lib.WKV7_ERR_INVALID
+    assert _bwd(_shape(reserved=1)) == _lib.WKV7_ERR_INVALID
+    # the chunk form needs N = 64 and C = 64
+    assert _bwd(_shape(N=16, algo=2)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert _bwd(_shape(chunk=32, algo=2)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert _bwd(_shape(chunk=128, algo=2)) == _lib.WKV7_ERR_UNSUPPORTED
     # workspace missing / too small / misaligned
     assert _bwd(sh) == _lib.WKV7_ERR_WORKSPACE
     need = _lib.lib().wkv7_backward_workspace_bytes(ctypes.byref(sh), 0)
@@ -105,13 +112,15 @@ def test_size_queries():
     # states every 64 steps, then the per-step sa tape
     ck = 8 * 32 * 64 * 64 * 64 * 4 + 8 * 4096 * 32 * 64 * 4
     assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == ck
-    # 7 sub-checkpoint slots of one chunk per (b, h)
-    assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) == 8 * 32 * 7 * 64 * 64 * 4
-    assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 0) == 8 * 32 * 7 * 64 * 64 * 4 + ck
+    # 7 sub-checkpoint slots of one chunk per (b, h), then one int per (b, h)
+    ws = 8 * 32 * 7 * 64 * 64 * 4 + 8 * 32 * 4
+    assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) == ws
+    assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 0) == ws + ck
     sh = _shape(B=1, T=65, H=1, N=16, chunk=8)
     # 9 states of 1 KiB (rounded up to 256 B) + 65 steps of sa
     assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == 9 * 16 * 16 * 4 + 65 * 16 * 4
-    assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) == 0
+    # no sub-checkpoints at C = 8; the flag ints round up to 256 bytes
+    assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) == 256
     assert L.wkv7_checkpoint_bytes(ctypes.byref(_shape(N=48))) == 0
     assert L.wkv7_checkpoint_bytes(None) == 0
 
