@@ -34,6 +34,8 @@
 // (b, h) in `flags`; the host then runs the step-by-step reverse scan for the
 // marked heads, which overwrites every output of those heads.
 
+#include <type_traits>
+
 #include "wkv7_device.h"
 #include "wkv7_internal.h"
 
@@ -103,6 +105,68 @@ __device__ __forceinline__ void row16(const float *s, int t, int c0, float (&o)[
     }
 }
 
+// Per-lane LDS offsets of the phase-2 access patterns, chosen so that the
+// block index only adds a constant (an instruction offset):
+//   col[s]  : element (16 ub + 4 g + s, jw) of a [64][64] array, minus 1024 ub
+//   rowb[m] : float4 (16 tb + l16, 16 g + 4 m .. +3), minus 1024 tb
+//   pa[s]   : Gram tile element (4 g + s, l16)
+//   pb      : Gram tile element (l16, 4 g) (then + s)
+//   hrow    : element (16 ub + 4 g + s, 16 (l16 / 4) + 4 ib + l16 % 4) minus
+//             1024 ub + 64 s + 4 (ib ^ s)
+struct LaneAddr {
+    int col[4], rowb[4], pa[4], pb, hrow;
+};
+
+__device__ __forceinline__ LaneAddr lane_addr(int l16, int g, int jw)
+{
+    LaneAddr a;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        a.col[s] = 64 * (4 * g + s) + ((((jw >> 2) ^ (4 * g + s)) & 15) << 2) + (jw & 3);
+        a.rowb[s] = 64 * l16 + ((((4 * g + s) ^ l16) & 15) << 2);
+        a.pa[s] = 64 * g + (((s + g) & 3) << 4) + l16;
+    }
+    a.pb = ((l16 >> 2) << 6) + ((((l16 & 3) + (l16 >> 2)) & 3) << 4) + 4 * g;
+    a.hrow = 256 * g + (((l16 >> 2) ^ g) << 4) + (l16 & 3);
+    return a;
+}
+
+// 16 floats of row 16 tb + l16 (columns 16 g ..) of a swizzled array
+__device__ __forceinline__ void rowl(const float *s, const LaneAddr &A, int tb, float (&o)[16])
+{
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float4 x = lds4(s, A.rowb[m] + 1024 * tb);
+        o[4 * m] = x.x;
+        o[4 * m + 1] = x.y;
+        o[4 * m + 2] = x.z;
+        o[4 * m + 3] = x.w;
+    }
+}
+
+// Keeps the scheduler from hoisting loads across this point (bounds the
+// registers held by operands in flight).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// X[tb] += rows 16 tb + l16 of the swizzled array sX (columns 16 g + s) times
+// bv[s], for tb = 0..3 (K = 64 over s and the row groups), two blocks at a time.
+__device__ __forceinline__ void rows_times(f4 (&X)[4], const float *sX, const LaneAddr &A,
+                                           const float (&bv)[16])
+{
+#pragma unroll
+    for (int h = 0; h < 4; h += 2) {
+        float x0[16], x1[16];
+        rowl(sX, A, h, x0);
+        rowl(sX, A, h + 1, x1);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            X[h] = mfma(x0[s], bv[s], X[h]);
+            X[h + 1] = mfma(x1[s], bv[s], X[h + 1]);
+        }
+        sched_fence();
+    }
+}
+
 template <typename TIn>
 struct BwdcArgs {
     const TIn *r, *w, *k, *v, *a, *b, *dy;
@@ -113,54 +177,69 @@ struct BwdcArgs {
     int nck;
 };
 
+// x from the lane of row-group G0 (lane >> 4 == G0) with the same lane & 15,
+// in every lane.  v_permlane16_swap(x, x) leaves the even row of each row
+// pair in its first result and the odd row in its second; v_permlane32_swap
+// does the same for the two halves of the wave.
+template <int G0>
+__device__ __forceinline__ float bcast_group(float x)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const unsigned y = (G0 & 1) ? p[1] : p[0];
+    const auto q = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+    return __builtin_bit_cast(float, (G0 & 2) ? q[1] : q[0]);
+}
+
 template <typename TIn>
 __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 {
     // chunk vectors, [step][feature] swizzled: cumulative decay, rb, ab, kt,
-    // bt, dsa, dy, and v (later sa)
+    // bt, dsa (Hb until dsa is known), dy, and v (later sa)
     __shared__ __align__(16) float sG[4096], sR[4096], sA[4096], sK[4096], sB[4096];
     __shared__ __align__(16) float sD[4096], sDY[4096], sVS[4096];
-    // Hb (a state, [row][col] swizzled) until phase 2 starts, then two Gram
-    // matrices (10 lower 16x16 tiles each)
+    // two Gram matrices (10 lower 16x16 tiles each)
     __shared__ __align__(16) float sP[20 * 256];
     __shared__ __align__(16) float sScan[4][256];
     __shared__ __align__(16) float sCp[4][64];
-    __shared__ __align__(16) float sC[64];
-    __shared__ float sBeta[68];
     __shared__ int sBad;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l16 = lane & 15, g = lane >> 4;
     const int64_t bh = blockIdx.x, T = p.T, H = p.H;
     const int64_t bb_ = bh / H, hh = bh % H;
     const int64_t stride = H * 64;
     const int64_t vbase = (bb_ * T * H + hh) * 64;
     const int nck = p.nck;
-    // phase 1: row prow of G, columns 16 pcg .. 16 pcg + 15
-    const int prow = wave * 16 + (lane >> 2), pcg = lane & 3;
-    // phase 2: feature jw of every output tile
-    const int jw = wave * 16 + l16;
+    // every phase-2 tile of this lane is in feature column jw; state
+    // gradients are held as rows 16 g + s (s = 4 ib + i) of column jw
+    int l16 = lane & 15, g = lane >> 4, jw = wave * 16 + (lane & 15);
+    // Makes the lane indices opaque again, so that the many LDS addresses
+    // derived from them are recomputed where they are used instead of being
+    // hoisted out of the chunk loop into (too many) registers.
+    LaneAddr A;
+    auto refresh = [&]() {
+        asm volatile("" : "+v"(l16), "+v"(g), "+v"(jw));
+        A = lane_addr(l16, g, jw);
+    };
 
-    float Gc[16];
-    if (p.dsT) {
+    // dL/dS at the end of the chunk being processed (rows 16 g + s, column jw)
+    f4 Hc[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float4 x = *reinterpret_cast<const float4 *>(p.dsT + bh * 4096 + prow * 64 + pcg * 16 + 4 * m);
-            Gc[4 * m] = x.x;
-            Gc[4 * m + 1] = x.y;
-            Gc[4 * m + 2] = x.z;
-            Gc[4 * m + 3] = x.w;
-        }
-    } else {
+    for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) Gc[q] = 0.f;
-    }
+        for (int i = 0; i < 4; ++i)
+            Hc[ib][i] = p.dsT ? p.dsT[bh * 4096 + (16 * g + 4 * ib + i) * 64 + jw] : 0.f;
     bool bad = false;
     if (tid == 0) sBad = 0;
 
     for (int c = nck - 1; c >= 0; --c) {
         const int64_t t0 = (int64_t)c * 64;
         const int Lc = (int)(T - t0 < 64 ? T - t0 : 64);
+        const float *S0 = p.ckpt + (bh * nck + c) * 4096;
+        // S0 column jw, rows 16 g + s
+        float s0B[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) s0B[s] = S0[(16 * g + s) * 64 + jw];
 
         // ---- stage r, w, k, a, b, v and dy for the chunk (zero past the end,
         // decay 1)
@@ -189,6 +268,7 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             put4(sDY, o, DY);
         }
         __syncthreads();
+        refresh();
 
         // ---- cumulative decay, in place of w: 4 segments of 16 steps per column
         {
@@ -199,6 +279,7 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             sCp[seg][j] = pr;
         }
         __syncthreads();
+        refresh();
         {
             const int j = tid & 63, seg = tid >> 6;
             float pre = 1.f;
@@ -213,8 +294,9 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             }
         }
         __syncthreads();
+        refresh();
 
-        // ---- rb = r g, ab = a g_prev, kt = k / g, bt = b / g
+        // ---- rb = r g, ab = a g_prev, kt = k / g, bt = b / g; Hb = H g_63
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int u = tid + 256 * m, t = u >> 4, j4 = (u & 15) << 2;
@@ -231,128 +313,158 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             x = lds4(sB, o);
             put4(sB, o, make_float4(x.x * inv.x, x.y * inv.y, x.z * inv.z, x.w * inv.w));
         }
-        __syncthreads();
-
-        // ---- beta_t = ab_t . bt_{t-1} (couples consecutive dsa), and Hb
-        {
-            const int t = tid >> 2, q = tid & 3;
-            float acc = 0.f;
-            if (t >= 1) {
+        const float g63 = sG[sw(63, jw)];
+        float hB[16];   // Hb column jw, rows 16 g + s
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const float4 x = lds4(sA, sw(t, 16 * q + 4 * m));
-                    const float4 y = lds4(sB, sw(t - 1, 16 * q + 4 * m));
-                    acc = fmaf(x.x, y.x, acc);
-                    acc = fmaf(x.y, y.y, acc);
-                    acc = fmaf(x.z, y.z, acc);
-                    acc = fmaf(x.w, y.w, acc);
-                }
-            }
-            acc = group_allreduce<4>(acc);
-            if (q == 0) sBeta[t] = acc;
-            if (tid == 0) sBeta[64] = 0.f;
-        }
-        {
-            float g63[16];
-            row16(sG, 63, 16 * pcg, g63);
-#pragma unroll
-            for (int q = 0; q < 16; ++q) Gc[q] *= g63[q];
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-                put4(sP, sw(prow, 16 * pcg + 4 * m),
-                     make_float4(Gc[4 * m], Gc[4 * m + 1], Gc[4 * m + 2], Gc[4 * m + 3]));
+        for (int s = 0; s < 16; ++s) {
+            hB[s] = Hc[s >> 2][s & 3] * g63;
+            sD[sw(16 * g + s, jw)] = hB[s];
         }
         __syncthreads();
+        refresh();
+        float hR[16];   // Hb row jw, columns 16 g + s
+        row16(sD, jw, 16 * g, hR);
 
-        // Hb column jw (rows 16 g ..) and row jw (columns 16 g ..): the B
-        // operands of its phase-2 products
-        float hB[16], hR[16];
+        // Gram tiles: slot n < 10 holds rows of sX1 times rows of sY, slot
+        // 10 + n rows of sX2 times rows of sY, for the lower block pair n
+        // (rows a of the first factor, b of the second); the diagonal block
+        // keeps a >= b for sX1 and a > b for sX2.  Wave w takes n = w + 4k,
+        // two tiles at a time.
+        auto gram_tile = [&](int n, const float *sX1, const float *sX2, const float *sY, f4 &acc) {
+            const int pr = n < 10 ? n : n - 10;
+            const int ab = tab(pr), bq = tbb(pr);
+            const float *sX = n < 10 ? sX1 : sX2;
+            float xv[16], yv[16];
+            rowl(sX, A, ab, xv);
+            rowl(sY, A, bq, yv);
+            f4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
 #pragma unroll
-        for (int s = 0; s < 16; ++s) hB[s] = sP[sw(16 * g + s, jw)];
-        row16(sP, jw, 16 * g, hR);
+            for (int s = 0; s < 16; s += 2) {
+                a0 = mfma(xv[s], yv[s], a0);
+                a1 = mfma(xv[s + 1], yv[s + 1], a1);
+            }
+            acc = a0 + a1;
+        };
+        auto gram_store = [&](int n, f4 acc) {
+            const int pr = n < 10 ? n : n - 10;
+            const bool diag = tab(pr) == tbb(pr);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int al = 4 * g + i;
+                float val = acc[i];
+                if (diag && (n < 10 ? al < l16 : al <= l16)) val = 0.f;
+                sP[n * 256 + A.pa[i]] = val;
+            }
+        };
+        auto gram = [&](const float *sX1, const float *sX2, const float *sY) {
+            f4 x0, x1;
+            gram_tile(wave, sX1, sX2, sY, x0);
+            gram_tile(wave + 4, sX1, sX2, sY, x1);
+            gram_store(wave, x0);
+            gram_store(wave + 4, x1);
+            gram_tile(wave + 8, sX1, sX2, sY, x0);
+            gram_tile(wave + 12, sX1, sX2, sY, x1);
+            gram_store(wave + 8, x0);
+            gram_store(wave + 12, x1);
+            gram_tile(wave + 16, sX1, sX2, sY, x0);
+            gram_store(wave + 16, x0);
+        };
+        // Gram tile slot elements (4 g + s, l16) and (l16, 4 g + s), and
+        // element (16 ub + 4 g + s, jw) of an array
+        auto tA = [&](int slot, int s) { return sP[slot * 256 + A.pa[s]]; };
+        auto tAt = [&](int slot, int s) { return sP[slot * 256 + A.pb + s]; };
+        auto colE = [&](const float *arr, int ub, int s) { return arr[A.col[s] + 1024 * ub]; };
 
-        // ---- phase 1: dsa_t = G_t b_t, last step first
-        {
-            float U[16];
-#pragma unroll
-            for (int q = 0; q < 16; ++q) U[q] = Gc[q];
-            float dsa1 = 0.f;   // dsa of the step after t, not yet folded into U
-            for (int t = Lc - 1; t >= 0; --t) {
-                const float dyv = sDY[sw(t, prow)];
-                float rv[16], bv[16];
-                row16(sR, t, 16 * pcg, rv);
-                row16(sB, t, 16 * pcg, bv);
-                float X[16];
-#pragma unroll
-                for (int q = 0; q < 16; ++q) X[q] = fmaf(dyv, rv[q], U[q]);
-                float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-                for (int q = 0; q < 16; q += 4) {
-                    s0 = fmaf(X[q], bv[q], s0);
-                    s1 = fmaf(X[q + 1], bv[q + 1], s1);
-                    s2 = fmaf(X[q + 2], bv[q + 2], s2);
-                    s3 = fmaf(X[q + 3], bv[q + 3], s3);
-                }
-                const float qs = group_allreduce<4>((s0 + s1) + (s2 + s3));
-                const float dsa = fmaf(dsa1, sBeta[t + 1], qs);
-                if (t + 1 < Lc) {
-                    float av[16];
-                    row16(sA, t + 1, 16 * pcg, av);
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) U[q] = fmaf(dsa1, av[q], X[q]);
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) U[q] = X[q];
-                }
-                dsa1 = dsa;
-                if (pcg == 0) sD[sw(t, prow)] = dsa;
-            }
-            float av[16];
-            row16(sA, 0, 16 * pcg, av);
-#pragma unroll
-            for (int q = 0; q < 16; ++q) Gc[q] = fmaf(dsa1, av[q], U[q]);   // dL/dS0
-        }
-        for (int u = tid; u < (64 - Lc) * 64; u += 256) sD[sw(Lc + (u >> 6), u & 63)] = 0.f;
-
-        // ---- c = column sums of dL/dS0 (.) S0; ds0 after the first chunk
-        const float *S0 = p.ckpt + (bh * nck + c) * 4096;
-        {
-            float x[16];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float4 s = *reinterpret_cast<const float4 *>(S0 + prow * 64 + pcg * 16 + 4 * m);
-                x[4 * m] = s.x * Gc[4 * m];
-                x[4 * m + 1] = s.y * Gc[4 * m + 1];
-                x[4 * m + 2] = s.z * Gc[4 * m + 2];
-                x[4 * m + 3] = s.w * Gc[4 * m + 3];
-            }
-            float y[8], z[4];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) y[q] = swap_add32(x[q], x[q + 8]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) z[q] = swap_add16(y[q], y[q + 4]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                z[q] += dpp<kDppRor4>(z[q]);
-                z[q] += dpp<kDppRor8>(z[q]);
-            }
-            if (((lane >> 2) & 3) == 0) {
-                const int col = 16 * pcg + 8 * ((lane >> 5) & 1) + 4 * ((lane >> 4) & 1);
-                *reinterpret_cast<float4 *>(&sCp[wave][col]) = make_float4(z[0], z[1], z[2], z[3]);
-            }
-            if (c == 0 && p.ds0) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    *reinterpret_cast<float4 *>(p.ds0 + bh * 4096 + prow * 64 + pcg * 16 + 4 * m) =
-                        make_float4(Gc[4 * m], Gc[4 * m + 1], Gc[4 * m + 2], Gc[4 * m + 3]);
-            }
-        }
-        // S0 column jw (rows 16 g ..)
-        float s0B[16];
-#pragma unroll
-        for (int s = 0; s < 16; ++s) s0B[s] = S0[(16 * g + s) * 64 + jw];
+        // ---- dsa for the chunk: dsa_t = rhs_t + sum_{u>t} dsa_u (ab_u . bt_t),
+        // rhs_t = Hb bt_t + sum_{u>=t} dy_u (rb_u . bt_t).  Rows i = jw,
+        // steps t = 16 tb + 4 g + i of f4 Rt[tb].
+        gram(sR, sA, sB);
         __syncthreads();
-        if (tid < 64) sC[tid] = (sCp[0][tid] + sCp[1][tid]) + (sCp[2][tid] + sCp[3][tid]);
+        refresh();
+        f4 Rt[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) Rt[tb] = f4{0.f, 0.f, 0.f, 0.f};
+        rows_times(Rt, sB, A, hR);
+#pragma unroll
+        for (int ub = 0; ub < 4; ++ub) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float bdy = colE(sDY, ub, s);
+#pragma unroll
+                for (int tb = 0; tb <= ub; ++tb) Rt[tb] = mfma(tA(tix(ub, tb), s), bdy, Rt[tb]);
+            }
+            sched_fence();
+        }
+        // blocked back substitution: the diagonal block step by step (each
+        // finished dsa broadcast to the row groups), then its contribution to
+        // the earlier blocks on MFMA
+        auto solve_block = [&](auto tbc) {
+            constexpr int tb = decltype(tbc)::value;
+            const int slot = 10 + tix(tb, tb);
+#pragma unroll
+            for (int tl = 15; tl >= 1; --tl) {
+                const float d = tl >= 12 ? bcast_group<3>(Rt[tb][tl & 3])
+                              : tl >= 8 ? bcast_group<2>(Rt[tb][tl & 3])
+                              : tl >= 4 ? bcast_group<1>(Rt[tb][tl & 3])
+                                        : bcast_group<0>(Rt[tb][tl & 3]);
+                const float4 m = lds4(sP, slot * 256 + pt(tl, 0) + 4 * g);
+                Rt[tb][0] = fmaf(m.x, d, Rt[tb][0]);
+                Rt[tb][1] = fmaf(m.y, d, Rt[tb][1]);
+                Rt[tb][2] = fmaf(m.z, d, Rt[tb][2]);
+                Rt[tb][3] = fmaf(m.w, d, Rt[tb][3]);
+            }
+#pragma unroll
+            for (int tp = 0; tp < tb; ++tp)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    Rt[tp] = mfma(tA(10 + tix(tb, tp), s), Rt[tb][s], Rt[tp]);
+        };
+        solve_block(std::integral_constant<int, 3>{});
+        solve_block(std::integral_constant<int, 2>{});
+        solve_block(std::integral_constant<int, 1>{});
+        solve_block(std::integral_constant<int, 0>{});
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tb + 4 * g + i;
+                sD[A.col[i] + 1024 * tb] = t < Lc ? Rt[tb][i] : 0.f;
+            }
+        __syncthreads();
+        refresh();
+
+        // ---- dL/dS before the chunk: Hb + sum_u dy_u rb_u^T + dsa_u ab_u^T
+        // (rows 16 g + s: the MFMA row m = l16 stands for row 16 (m / 4) + 4 ib + m % 4)
+        {
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Hc[ib][i] = hB[4 * ib + i];
+#pragma unroll
+            for (int ub = 0; ub < 4; ++ub) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                        const float br = colE(sR, ub, s), ba = colE(sA, ub, s);
+#pragma unroll
+                    for (int ib = 0; ib < 4; ++ib) {
+                        const int o = A.hrow + 1024 * ub + 64 * s + 4 * (ib ^ s);
+                        Hc[ib] = mfma(sDY[o], br, Hc[ib]);
+                        Hc[ib] = mfma(sD[o], ba, Hc[ib]);
+                    }
+                }
+                sched_fence();
+            }
+        }
+        // c_j = sum_i (dL/dS0)[i][j] S0[i][j]; ds0 after the first chunk
+        float cj = 0.f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) cj = fmaf(Hc[s >> 2][s & 3], s0B[s], cj);
+        cj = swap_add16(cj, cj);
+        cj = swap_add32(cj, cj);
+        if (c == 0 && p.ds0) {
+#pragma unroll
+            for (int s = 0; s < 16; ++s) p.ds0[bh * 4096 + (16 * g + s) * 64 + jw] = Hc[s >> 2][s & 3];
+        }
 
         // sa for the second pass, loaded while the first one runs
         float4 saR[4];
@@ -363,32 +475,6 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 
-        // Gram tiles: slot n < 10 holds rows of sX1 times rows of sY, slot
-        // 10 + n rows of sX2 times rows of sY, for the lower block pair n
-        // (rows a of the first factor, b of the second); the diagonal block
-        // keeps a >= b for sX1 and a > b for sX2.  Wave w takes n = w + 4k.
-        auto gram = [&](const float *sX1, const float *sX2, const float *sY) {
-#pragma unroll 1
-            for (int n = wave; n < 20; n += 4) {
-                const int pr = n < 10 ? n : n - 10;
-                const int ab = tab(pr), bq = tbb(pr);
-                const float *sX = n < 10 ? sX1 : sX2;
-                float xv[16], yv[16];
-                row16(sX, 16 * ab + l16, 16 * g, xv);
-                row16(sY, 16 * bq + l16, 16 * g, yv);
-                f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 16; ++s) acc = mfma(xv[s], yv[s], acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int al = 4 * g + i;
-                    float val = acc[i];
-                    if (ab == bq && (n < 10 ? al < l16 : al <= l16)) val = 0.f;
-                    sP[n * 256 + pt(al, l16)] = val;
-                }
-            }
-        };
-
         f4 XR[4], XA[4], XK[4], XB[4], XV[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
@@ -398,102 +484,76 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             XB[tb] = XR[tb];
             XV[tb] = XR[tb];
         }
-        // dk / db bracket: Hb term with the value rows in sVS, then the Gram
-        // terms over u >= t with rb and ab.
-        auto back_terms = [&](f4 (&X)[4]) {
+        // One pass over the Grams of the value-side vectors in sVS (v, then
+        // sa): X (dk, then db bracket) gets Hb^T x_t + sum_{u>=t} rb_u (dy_u.x_t)
+        // + sum_{u>t} ab_u (dsa_u.x_t); the dr, da brackets get
+        // sum_{u<=t} f_u (x_u.dy_t) and sum_{u<t} f_u (x_u.dsa_t) with the
+        // key-side vector sF (kt, then bt).
+        auto value_pass = [&](f4 (&X)[4], const float *sF) {
+            rows_times(X, sVS, A, hB);
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                float va[16];
-                row16(sVS, 16 * tb + l16, 16 * g, va);
+            for (int ub = 0; ub < 4; ++ub)
 #pragma unroll
-                for (int s = 0; s < 16; ++s) X[tb] = mfma(va[s], hB[s], X[tb]);
-#pragma unroll 1
-                for (int ub = tb; ub < 4; ++ub) {
-                    const int slot = tix(ub, tb);
+                for (int s = 0; s < 4; ++s) {
+                    if (s == 2) sched_fence();
+                        const float br = colE(sR, ub, s), ba = colE(sA, ub, s), bf = colE(sF, ub, s);
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const int u = 16 * ub + 4 * g + s;
-                        const float a1 = sP[slot * 256 + pt(4 * g + s, l16)];
-                        const float a2 = sP[(10 + slot) * 256 + pt(4 * g + s, l16)];
-                        X[tb] = mfma(a1, sR[sw(u, jw)], X[tb]);
-                        X[tb] = mfma(a2, sA[sw(u, jw)], X[tb]);
+                    for (int tb = 0; tb <= ub; ++tb) {
+                        X[tb] = mfma(tA(tix(ub, tb), s), br, X[tb]);
+                        X[tb] = mfma(tA(10 + tix(ub, tb), s), ba, X[tb]);
                     }
-                }
-            }
-        };
-        // dr / da brackets: Gram terms over u <= t with the key-side vector
-        // sF (kt with the v Grams, bt with the sa Grams).
-        auto fwd_terms = [&](const float *sF) {
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll 1
-                for (int ub = 0; ub <= tb; ++ub) {
-                    const int slot = tix(tb, ub);
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const int u = 16 * ub + 4 * g + s;
-                        const float a1 = sP[slot * 256 + pt(l16, 4 * g + s)];
-                        const float a2 = sP[(10 + slot) * 256 + pt(l16, 4 * g + s)];
-                        const float bf = sF[sw(u, jw)];
-                        XR[tb] = mfma(a1, bf, XR[tb]);
-                        XA[tb] = mfma(a2, bf, XA[tb]);
+                    for (int tb = ub; tb < 4; ++tb) {
+                        XR[tb] = mfma(tAt(tix(tb, ub), s), bf, XR[tb]);
+                        XA[tb] = mfma(tAt(10 + tix(tb, ub), s), bf, XA[tb]);
                     }
+                    if (s == 3) sched_fence();
                 }
-            }
         };
 
         // ---- pass 1: Grams dy v^T, dsa v^T; dk bracket; S0 and kt terms of dr, da
         gram(sDY, sD, sVS);
         __syncthreads();
-        back_terms(XK);
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            float ya[16], da_[16];
-            row16(sDY, 16 * tb + l16, 16 * g, ya);
-            row16(sD, 16 * tb + l16, 16 * g, da_);
-#pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                XR[tb] = mfma(ya[s], s0B[s], XR[tb]);
-                XA[tb] = mfma(da_[s], s0B[s], XA[tb]);
-            }
-        }
-        fwd_terms(sK);
+        refresh();
+        value_pass(XK, sK);
+        rows_times(XR, sDY, A, s0B);
+        rows_times(XA, sD, A, s0B);
         __syncthreads();
+        refresh();
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int u = tid + 256 * m, t = u >> 4, j4 = (u & 15) << 2;
             put4(sVS, sw(t, j4), saR[m]);
         }
         __syncthreads();
+        refresh();
 
         // ---- pass 2: Grams dy sa^T, dsa sa^T; db bracket; bt terms of dr, da
         gram(sDY, sD, sVS);
         __syncthreads();
-        back_terms(XB);
-        fwd_terms(sB);
+        refresh();
+        value_pass(XB, sB);
         __syncthreads();
+        refresh();
 
-        // ---- pass 3: Grams rb kt^T, ab kt^T; dv
+        // ---- pass 3: Grams rb kt^T, ab kt^T; dv = Hb kt_t + sum_{u>=t} dy_u
+        // (rb_u . kt_t) + sum_{u>t} dsa_u (ab_u . kt_t)
         gram(sR, sA, sK);
         __syncthreads();
+        refresh();
+        rows_times(XV, sK, A, hR);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            float ka[16];
-            row16(sK, 16 * tb + l16, 16 * g, ka);
+        for (int ub = 0; ub < 4; ++ub) {
 #pragma unroll
-            for (int s = 0; s < 16; ++s) XV[tb] = mfma(ka[s], hR[s], XV[tb]);
-#pragma unroll 1
-            for (int ub = tb; ub < 4; ++ub) {
-                const int slot = tix(ub, tb);
+            for (int s = 0; s < 4; ++s) {
+                const float bdy = colE(sDY, ub, s), bd = colE(sD, ub, s);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int u = 16 * ub + 4 * g + s;
-                    const float a1 = sP[slot * 256 + pt(4 * g + s, l16)];
-                    const float a2 = sP[(10 + slot) * 256 + pt(4 * g + s, l16)];
-                    XV[tb] = mfma(a1, sDY[sw(u, jw)], XV[tb]);
-                    XV[tb] = mfma(a2, sD[sw(u, jw)], XV[tb]);
+                for (int tb = 0; tb <= ub; ++tb) {
+                    XV[tb] = mfma(tA(tix(ub, tb), s), bdy, XV[tb]);
+                    XV[tb] = mfma(tA(10 + tix(ub, tb), s), bd, XV[tb]);
                 }
             }
+            sched_fence();
         }
 
         // ---- outputs and dw (prefix over steps of k dk + b db - r dr - a da)
@@ -503,7 +563,7 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int o = sw(16 * tb + 4 * g + i, jw);
+                    const int o = A.col[i] + 1024 * tb;
                     f[tb][i] = sK[o] * XK[tb][i] + sB[o] * XB[tb][i] - sR[o] * XR[tb][i] -
                                sA[o] * XA[tb][i];
                 }
@@ -513,7 +573,6 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             float blk[16];
 #pragma unroll
             for (int q = 0; q < 16; ++q) blk[q] = sScan[wave][q * 16 + l16];
-            const float cj = sC[jw];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 float ex = 0.f;
@@ -523,9 +582,9 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = 16 * tb + 4 * g + i;
-                    const int o = sw(t, jw);
+                    const int o = A.col[i] + 1024 * tb;
                     const float gt = sG[o];
-                    const float gp = t > 0 ? sG[sw(t - 1, jw)] : 1.f;
+                    const float gp = i > 0 ? sG[A.col[i - 1] + 1024 * tb] : t > 0 ? sG[sw(t - 1, jw)] : 1.f;
                     const float inv = 1.f / gt;
                     const float adA = sA[o] * XA[tb][i];
                     const float wdw = (cj + ex) - adA;
@@ -543,6 +602,7 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             }
         }
         __syncthreads();
+        refresh();
     }
 
     if (bad) sBad = 1;
