@@ -148,23 +148,34 @@ __device__ __forceinline__ void rowl(const float *s, const LaneAddr &A, int tb, 
 // registers held by operands in flight).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Runs mma(k, buf) for k = 0 .. N-1 with the operands of group k loaded by
+// load(k, buf) one group ahead into the other of two register buffers, so
+// that each group's LDS reads are in flight while the previous group's
+// MFMAs run.
+template <int N, int W, typename L, typename M>
+__device__ __forceinline__ void pipelined(L load, M mma)
+{
+    float buf[2][W];
+    load(0, buf[0]);
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        sched_fence();
+        if (k + 1 < N) load(k + 1, buf[(k + 1) & 1]);
+        mma(k, buf[k & 1]);
+    }
+    sched_fence();
+}
+
 // X[tb] += rows 16 tb + l16 of the swizzled array sX (columns 16 g + s) times
-// bv[s], for tb = 0..3 (K = 64 over s and the row groups), two blocks at a time.
+// bv[s], for tb = 0..3 (K = 64 over s and the row groups).
 __device__ __forceinline__ void rows_times(f4 (&X)[4], const float *sX, const LaneAddr &A,
                                            const float (&bv)[16])
 {
+    pipelined<4, 16>([&](int tb, float (&b)[16]) { rowl(sX, A, tb, b); },
+                     [&](int tb, const float (&b)[16]) {
 #pragma unroll
-    for (int h = 0; h < 4; h += 2) {
-        float x0[16], x1[16];
-        rowl(sX, A, h, x0);
-        rowl(sX, A, h + 1, x1);
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            X[h] = mfma(x0[s], bv[s], X[h]);
-            X[h + 1] = mfma(x1[s], bv[s], X[h + 1]);
-        }
-        sched_fence();
-    }
+                         for (int s = 0; s < 16; ++s) X[tb] = mfma(b[s], bv[s], X[tb]);
+                     });
 }
 
 template <typename TIn>
@@ -204,7 +215,8 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
     __shared__ __align__(16) float sCp[4][64];
     __shared__ int sBad;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t bh = blockIdx.x, T = p.T, H = p.H;
     const int64_t bb_ = bh / H, hh = bh % H;
     const int64_t stride = H * 64;
@@ -229,43 +241,79 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             Hc[ib][i] = p.dsT ? p.dsT[bh * 4096 + (16 * g + 4 * ib + i) * 64 + jw] : 0.f;
-    bool bad = false;
     if (tid == 0) sBad = 0;
 
-    for (int c = nck - 1; c >= 0; --c) {
-        const int64_t t0 = (int64_t)c * 64;
-        const int Lc = (int)(T - t0 < 64 ? T - t0 : 64);
-        const float *S0 = p.ckpt + (bh * nck + c) * 4096;
-        // S0 column jw, rows 16 g + s
-        float s0B[16];
+    // The inputs of a chunk (r, w, k, a, b, v, dy) and its checkpoint's
+    // column jw (rows 16 g + s) are loaded one chunk ahead, during the
+    // previous chunk's last pass.  Every chunk but the last is full.  fp32
+    // r, w, a, b, v go straight to their LDS arrays (free by then); k and dy,
+    // and all bf16 inputs (widened on the way into LDS), go through
+    // registers: 4 float4 units per thread and input.
+    using Raw = typename InQuad<TIn>::raw;
+    constexpr bool kDma = std::is_same<TIn, float>::value;
+    Raw pre[7][4];
+    float s0B[16];
+    const TIn *src_[7] = {p.r, p.w, p.k, p.a, p.b, p.v, p.dy};
+    float *dst_[7] = {sR, sG, sK, sA, sB, sVS, sDY};
+    auto chunk_len = [&](int cc) {
+        const int64_t rem = T - (int64_t)cc * 64;
+        return (int)(rem < 64 ? rem : 64);
+    };
+    auto issue_s0 = [&](int cc) {
+        const float *S0n = p.ckpt + (bh * nck + cc) * 4096;
 #pragma unroll
-        for (int s = 0; s < 16; ++s) s0B[s] = S0[(16 * g + s) * 64 + jw];
-
-        // ---- stage r, w, k, a, b, v and dy for the chunk (zero past the end,
-        // decay 1)
+        for (int s = 0; s < 16; ++s) s0B[s] = S0n[(16 * g + s) * 64 + jw];
+    };
+    auto issue_regs = [&](int cc, int q) {
+        const int64_t tt0 = (int64_t)cc * 64;
+        const int Lcc = chunk_len(cc);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int u = tid + 256 * m, t = u >> 4, j4 = (u & 15) << 2;
-            float4 R = make_float4(0.f, 0.f, 0.f, 0.f), W = make_float4(1.f, 1.f, 1.f, 1.f);
-            float4 K = R, A = R, Bv = R, V = R, DY = R;
-            if (t < Lc) {
-                const int64_t off = vbase + (t0 + t) * stride + j4;
-                R = ld4(p.r + off);
-                W = ld4(p.w + off);
-                K = ld4(p.k + off);
-                A = ld4(p.a + off);
-                Bv = ld4(p.b + off);
-                V = ld4(p.v + off);
-                DY = ld4(p.dy + off);
-            }
-            const int o = sw(t, j4);
-            put4(sR, o, R);
-            put4(sG, o, W);
-            put4(sK, o, K);
-            put4(sA, o, A);
-            put4(sB, o, Bv);
-            put4(sVS, o, V);
-            put4(sDY, o, DY);
+            if (t < Lcc) pre[q][m] = InQuad<TIn>::load(src_[q] + vbase + (tt0 + t) * stride + j4);
+        }
+    };
+    auto commit_regs = [&](int Lcc, int q) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int u = tid + 256 * m, t = u >> 4, j4 = (u & 15) << 2;
+            const float d = q == 1 ? 1.f : 0.f;
+            put4(dst_[q], sw(t, j4), t < Lcc ? InQuad<TIn>::f32(pre[q][m]) : make_float4(d, d, d, d));
+        }
+    };
+    // one full chunk of input q straight into its LDS array: 1 KB (4 rows)
+    // per wave instruction, lane l landing at float 4 l of the block, i.e.
+    // row 4 blk + l / 16, swizzled column group l % 16
+    auto issue_dma = [&](int cc, int q) {
+        const int64_t tt0 = (int64_t)cc * 64;
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+            const int blk = wave + 4 * k4;
+            const int t = 4 * blk + (lane >> 4);
+            const int j4 = ((lane & 15) ^ (t & 15)) << 2;
+            dma16(reinterpret_cast<const float *>(src_[q]) + vbase + (tt0 + t) * stride + j4,
+                  dst_[q] + blk * 256);
+        }
+    };
+    {
+        const int cl = nck - 1, Ll = chunk_len(cl);
+#pragma unroll
+        for (int q = 0; q < 7; ++q) issue_regs(cl, q);
+        issue_s0(cl);
+#pragma unroll
+        for (int q = 0; q < 7; ++q) commit_regs(Ll, q);
+    }
+
+    for (int c = nck - 1; c >= 0; --c) {
+        const int64_t t0 = (int64_t)c * 64;
+        const int Lc = chunk_len(c);
+
+        // ---- inputs of the chunk into LDS (the last chunk is there already)
+        if (c != nck - 1) {
+#pragma unroll
+            for (int q = 0; q < 7; ++q)
+                if (!kDma || q == 2 || q == 6) commit_regs(64, q);
+            if (kDma) wait_dma();
         }
         __syncthreads();
         refresh();
@@ -284,14 +332,16 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             const int j = tid & 63, seg = tid >> 6;
             float pre = 1.f;
             for (int s2 = 0; s2 < seg; ++s2) pre *= sCp[s2][j];
+            bool ok = true;
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const int o = sw(seg * 16 + u, j);
                 const float wv = sG[o];
                 pre *= wv;
-                bad |= !(wv >= kWMin && wv <= 1.f && pre >= kGMin);
+                ok = ok && wv >= kWMin && wv <= 1.f && pre >= kGMin;
                 sG[o] = pre;
             }
+            if (!ok) sBad = 1;   // every writer stores 1
         }
         __syncthreads();
         refresh();
@@ -329,22 +379,8 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         // 10 + n rows of sX2 times rows of sY, for the lower block pair n
         // (rows a of the first factor, b of the second); the diagonal block
         // keeps a >= b for sX1 and a > b for sX2.  Wave w takes n = w + 4k,
-        // two tiles at a time.
-        auto gram_tile = [&](int n, const float *sX1, const float *sX2, const float *sY, f4 &acc) {
-            const int pr = n < 10 ? n : n - 10;
-            const int ab = tab(pr), bq = tbb(pr);
-            const float *sX = n < 10 ? sX1 : sX2;
-            float xv[16], yv[16];
-            rowl(sX, A, ab, xv);
-            rowl(sY, A, bq, yv);
-            f4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-#pragma unroll
-            for (int s = 0; s < 16; s += 2) {
-                a0 = mfma(xv[s], yv[s], a0);
-                a1 = mfma(xv[s + 1], yv[s + 1], a1);
-            }
-            acc = a0 + a1;
-        };
+        // k = 0..4, loading tile k + 1 while the MFMAs of tile k run; side(k)
+        // is independent work placed beside tile k's MFMAs.
         auto gram_store = [&](int n, f4 acc) {
             const int pr = n < 10 ? n : n - 10;
             const bool diag = tab(pr) == tbb(pr);
@@ -356,19 +392,40 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                 sP[n * 256 + A.pa[i]] = val;
             }
         };
-        auto gram = [&](const float *sX1, const float *sX2, const float *sY) {
-            f4 x0, x1;
-            gram_tile(wave, sX1, sX2, sY, x0);
-            gram_tile(wave + 4, sX1, sX2, sY, x1);
-            gram_store(wave, x0);
-            gram_store(wave + 4, x1);
-            gram_tile(wave + 8, sX1, sX2, sY, x0);
-            gram_tile(wave + 12, sX1, sX2, sY, x1);
-            gram_store(wave + 8, x0);
-            gram_store(wave + 12, x1);
-            gram_tile(wave + 16, sX1, sX2, sY, x0);
-            gram_store(wave + 16, x0);
+        auto gram = [&](const float *sX1, const float *sX2, const float *sY, auto side) {
+            float xa[16], ya[16], xb[16], yb[16];
+            auto load = [&](int n, float (&xv)[16], float (&yv)[16]) {
+                const int pr = n < 10 ? n : n - 10;
+                rowl(n < 10 ? sX1 : sX2, A, tab(pr), xv);
+                rowl(sY, A, tbb(pr), yv);
+            };
+            auto run = [&](int n, const float (&xv)[16], const float (&yv)[16]) {
+                f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 16; ++s) acc = mfma(xv[s], yv[s], acc);
+                gram_store(n, acc);
+            };
+            load(wave, xa, ya);
+            load(wave + 4, xb, yb);
+            side(0);
+            run(wave, xa, ya);
+            sched_fence();
+            load(wave + 8, xa, ya);
+            side(1);
+            run(wave + 4, xb, yb);
+            sched_fence();
+            load(wave + 12, xb, yb);
+            side(2);
+            run(wave + 8, xa, ya);
+            sched_fence();
+            load(wave + 16, xa, ya);
+            side(3);
+            run(wave + 12, xb, yb);
+            sched_fence();
+            side(4);
+            run(wave + 16, xa, ya);
         };
+        auto none = [](int) {};
         // Gram tile slot elements (4 g + s, l16) and (l16, 4 g + s), and
         // element (16 ub + 4 g + s, jw) of an array
         auto tA = [&](int slot, int s) { return sP[slot * 256 + A.pa[s]]; };
@@ -378,23 +435,25 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         // ---- dsa for the chunk: dsa_t = rhs_t + sum_{u>t} dsa_u (ab_u . bt_t),
         // rhs_t = Hb bt_t + sum_{u>=t} dy_u (rb_u . bt_t).  Rows i = jw,
         // steps t = 16 tb + 4 g + i of f4 Rt[tb].
-        gram(sR, sA, sB);
+        gram(sR, sA, sB, none);
         __syncthreads();
         refresh();
         f4 Rt[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) Rt[tb] = f4{0.f, 0.f, 0.f, 0.f};
         rows_times(Rt, sB, A, hR);
+        pipelined<16, 5>(
+            [&](int k, float (&b)[5]) {
+                const int ub = k >> 2, s = k & 3;
+                b[0] = colE(sDY, ub, s);
 #pragma unroll
-        for (int ub = 0; ub < 4; ++ub) {
+                for (int tb = 0; tb <= ub; ++tb) b[1 + tb] = tA(tix(ub, tb), s);
+            },
+            [&](int k, const float (&b)[5]) {
+                const int ub = k >> 2;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const float bdy = colE(sDY, ub, s);
-#pragma unroll
-                for (int tb = 0; tb <= ub; ++tb) Rt[tb] = mfma(tA(tix(ub, tb), s), bdy, Rt[tb]);
-            }
-            sched_fence();
-        }
+                for (int tb = 0; tb <= ub; ++tb) Rt[tb] = mfma(b[1 + tb], b[0], Rt[tb]);
+            });
         // blocked back substitution: the diagonal block step by step (each
         // finished dsa broadcast to the row groups), then its contribution to
         // the earlier blocks on MFMA
@@ -440,20 +499,25 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) Hc[ib][i] = hB[4 * ib + i];
-#pragma unroll
-            for (int ub = 0; ub < 4; ++ub) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                        const float br = colE(sR, ub, s), ba = colE(sA, ub, s);
+            pipelined<16, 10>(
+                [&](int k, float (&b)[10]) {
+                    const int ub = k >> 2, s = k & 3;
+                    b[0] = colE(sR, ub, s);
+                    b[1] = colE(sA, ub, s);
 #pragma unroll
                     for (int ib = 0; ib < 4; ++ib) {
                         const int o = A.hrow + 1024 * ub + 64 * s + 4 * (ib ^ s);
-                        Hc[ib] = mfma(sDY[o], br, Hc[ib]);
-                        Hc[ib] = mfma(sD[o], ba, Hc[ib]);
+                        b[2 + 2 * ib] = sDY[o];
+                        b[3 + 2 * ib] = sD[o];
                     }
-                }
-                sched_fence();
-            }
+                },
+                [&](int k, const float (&b)[10]) {
+#pragma unroll
+                    for (int ib = 0; ib < 4; ++ib) {
+                        Hc[ib] = mfma(b[2 + 2 * ib], b[0], Hc[ib]);
+                        Hc[ib] = mfma(b[3 + 2 * ib], b[1], Hc[ib]);
+                    }
+                });
         }
         // c_j = sum_i (dL/dS0)[i][j] S0[i][j]; ds0 after the first chunk
         float cj = 0.f;
@@ -475,14 +539,13 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 
-        f4 XR[4], XA[4], XK[4], XB[4], XV[4];
+        f4 XR[4], XA[4], XK[4], XB[4];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
             XR[tb] = f4{0.f, 0.f, 0.f, 0.f};
             XA[tb] = XR[tb];
             XK[tb] = XR[tb];
             XB[tb] = XR[tb];
-            XV[tb] = XR[tb];
         }
         // One pass over the Grams of the value-side vectors in sVS (v, then
         // sa): X (dk, then db bracket) gets Hb^T x_t + sum_{u>=t} rb_u (dy_u.x_t)
@@ -491,28 +554,45 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         // key-side vector sF (kt, then bt).
         auto value_pass = [&](f4 (&X)[4], const float *sF) {
             rows_times(X, sVS, A, hB);
-#pragma unroll
-            for (int ub = 0; ub < 4; ++ub)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    if (s == 2) sched_fence();
-                        const float br = colE(sR, ub, s), ba = colE(sA, ub, s), bf = colE(sF, ub, s);
+            // per group (ub, s): br, ba, bf, then the A operands in MFMA order
+            pipelined<16, 13>(
+                [&](int k, float (&b)[13]) {
+                    const int ub = k >> 2, s = k & 3;
+                    b[0] = colE(sR, ub, s);
+                    b[1] = colE(sA, ub, s);
+                    b[2] = colE(sF, ub, s);
+                    int n = 3;
 #pragma unroll
                     for (int tb = 0; tb <= ub; ++tb) {
-                        X[tb] = mfma(tA(tix(ub, tb), s), br, X[tb]);
-                        X[tb] = mfma(tA(10 + tix(ub, tb), s), ba, X[tb]);
+                        b[n++] = tA(tix(ub, tb), s);
+                        b[n++] = tA(10 + tix(ub, tb), s);
                     }
 #pragma unroll
                     for (int tb = ub; tb < 4; ++tb) {
-                        XR[tb] = mfma(tAt(tix(tb, ub), s), bf, XR[tb]);
-                        XA[tb] = mfma(tAt(10 + tix(tb, ub), s), bf, XA[tb]);
+                        b[n++] = tAt(tix(tb, ub), s);
+                        b[n++] = tAt(10 + tix(tb, ub), s);
                     }
-                    if (s == 3) sched_fence();
-                }
+                },
+                [&](int k, const float (&b)[13]) {
+                    const int ub = k >> 2;
+                    int n = 3;
+#pragma unroll
+                    for (int tb = 0; tb <= ub; ++tb) {
+                        X[tb] = mfma(b[n], b[0], X[tb]);
+                        X[tb] = mfma(b[n + 1], b[1], X[tb]);
+                        n += 2;
+                    }
+#pragma unroll
+                    for (int tb = ub; tb < 4; ++tb) {
+                        XR[tb] = mfma(b[n], b[2], XR[tb]);
+                        XA[tb] = mfma(b[n + 1], b[2], XA[tb]);
+                        n += 2;
+                    }
+                });
         };
 
         // ---- pass 1: Grams dy v^T, dsa v^T; dk bracket; S0 and kt terms of dr, da
-        gram(sDY, sD, sVS);
+        gram(sDY, sD, sVS, none);
         __syncthreads();
         refresh();
         value_pass(XK, sK);
@@ -529,83 +609,109 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         refresh();
 
         // ---- pass 2: Grams dy sa^T, dsa sa^T; db bracket; bt terms of dr, da
-        gram(sDY, sD, sVS);
+        gram(sDY, sD, sVS, none);
         __syncthreads();
         refresh();
         value_pass(XB, sB);
         __syncthreads();
         refresh();
 
-        // ---- pass 3: Grams rb kt^T, ab kt^T; dv = Hb kt_t + sum_{u>=t} dy_u
-        // (rb_u . kt_t) + sum_{u>t} dsa_u (ab_u . kt_t)
-        gram(sR, sA, sK);
+        // ---- outputs dk, db, dr, da, dw (dw: prefix over steps of
+        // k dk + b db - r dr - a da), beside the pass-3 Grams rb kt^T, ab kt^T
+        const int64_t cb = vbase + t0 * stride;   // this chunk's outputs
+        float *odk = p.dk + cb, *odb = p.db + cb, *odr = p.dr + cb;
+        float *oda = p.da + cb, *odw = p.dw + cb, *odv = p.dv + cb;
+        float f[4][4], blk[16];
+        auto outputs = [&](int k) {
+            if (k == 0) {
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int o = A.col[i] + 1024 * tb;
+                        f[tb][i] = sK[o] * XK[tb][i] + sB[o] * XB[tb][i] - sR[o] * XR[tb][i] -
+                                   sA[o] * XA[tb][i];
+                    }
+                    sScan[wave][(4 * tb + g) * 16 + l16] = ((f[tb][0] + f[tb][1]) + f[tb][2]) + f[tb][3];
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int q = 0; q < 16; ++q) blk[q] = sScan[wave][q * 16 + l16];
+                return;
+            }
+            const int tb = k - 1;
+            float ex = 0.f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (q < 4 * tb + g) ex += blk[q];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tb + 4 * g + i;
+                const int o = A.col[i] + 1024 * tb;
+                const float gt = sG[o];
+                const float gp = i > 0 ? sG[A.col[i - 1] + 1024 * tb] : t > 0 ? sG[sw(t - 1, jw)] : 1.f;
+                const float inv = __builtin_amdgcn_rcpf(gt);
+                const float adA = sA[o] * XA[tb][i];
+                const float wdw = (cj + ex) - adA;
+                if (t < Lc) {
+                    const int off = t * (int)stride + jw;
+                    odk[off] = XK[tb][i] * inv;
+                    odb[off] = XB[tb][i] * inv;
+                    odr[off] = XR[tb][i] * gt;
+                    oda[off] = XA[tb][i] * gp;
+                    odw[off] = wdw * gp * inv;
+                }
+                ex += f[tb][i];
+            }
+        };
+        gram(sR, sA, sK, outputs);
         __syncthreads();
         refresh();
+        if (c > 0) {
+#pragma unroll
+            for (int q = 0; q < 7; ++q) {
+                if (kDma && q != 2 && q != 6) issue_dma(c - 1, q);
+                else issue_regs(c - 1, q);
+            }
+            issue_s0(c - 1);
+        }
+        sched_fence();
+
+        // ---- dv = Hb kt_t + sum_{u>=t} dy_u (rb_u . kt_t) + sum_{u>t} dsa_u (ab_u . kt_t)
+        f4 XV[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) XV[tb] = f4{0.f, 0.f, 0.f, 0.f};
         rows_times(XV, sK, A, hR);
-#pragma unroll
-        for (int ub = 0; ub < 4; ++ub) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const float bdy = colE(sDY, ub, s), bd = colE(sD, ub, s);
+        pipelined<16, 10>(
+            [&](int k, float (&b)[10]) {
+                const int ub = k >> 2, s = k & 3;
+                b[0] = colE(sDY, ub, s);
+                b[1] = colE(sD, ub, s);
 #pragma unroll
                 for (int tb = 0; tb <= ub; ++tb) {
-                    XV[tb] = mfma(tA(tix(ub, tb), s), bdy, XV[tb]);
-                    XV[tb] = mfma(tA(10 + tix(ub, tb), s), bd, XV[tb]);
+                    b[2 + 2 * tb] = tA(tix(ub, tb), s);
+                    b[3 + 2 * tb] = tA(10 + tix(ub, tb), s);
                 }
-            }
-            sched_fence();
-        }
-
-        // ---- outputs and dw (prefix over steps of k dk + b db - r dr - a da)
-        {
-            float f[4][4];
+            },
+            [&](int k, const float (&b)[10]) {
+                const int ub = k >> 2;
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int o = A.col[i] + 1024 * tb;
-                    f[tb][i] = sK[o] * XK[tb][i] + sB[o] * XB[tb][i] - sR[o] * XR[tb][i] -
-                               sA[o] * XA[tb][i];
+                for (int tb = 0; tb <= ub; ++tb) {
+                    XV[tb] = mfma(b[2 + 2 * tb], b[0], XV[tb]);
+                    XV[tb] = mfma(b[3 + 2 * tb], b[1], XV[tb]);
                 }
-                sScan[wave][(4 * tb + g) * 16 + l16] = ((f[tb][0] + f[tb][1]) + f[tb][2]) + f[tb][3];
+            });
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tb + 4 * g + i;
+                if (t < Lc) odv[t * (int)stride + jw] = XV[tb][i];
             }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            float blk[16];
-#pragma unroll
-            for (int q = 0; q < 16; ++q) blk[q] = sScan[wave][q * 16 + l16];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                float ex = 0.f;
-#pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    if (q < 4 * tb + g) ex += blk[q];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * tb + 4 * g + i;
-                    const int o = A.col[i] + 1024 * tb;
-                    const float gt = sG[o];
-                    const float gp = i > 0 ? sG[A.col[i - 1] + 1024 * tb] : t > 0 ? sG[sw(t - 1, jw)] : 1.f;
-                    const float inv = 1.f / gt;
-                    const float adA = sA[o] * XA[tb][i];
-                    const float wdw = (cj + ex) - adA;
-                    if (t < Lc) {
-                        const int64_t off = vbase + (t0 + t) * stride + jw;
-                        p.dk[off] = XK[tb][i] * inv;
-                        p.db[off] = XB[tb][i] * inv;
-                        p.dr[off] = XR[tb][i] * gt;
-                        p.da[off] = XA[tb][i] * gp;
-                        p.dw[off] = wdw * gp * inv;
-                        p.dv[off] = XV[tb][i];
-                    }
-                    ex += f[tb][i];
-                }
-            }
-        }
         __syncthreads();
         refresh();
     }
 
-    if (bad) sBad = 1;
     __syncthreads();
     if (tid == 0) p.flags[bh] = sBad;
 }

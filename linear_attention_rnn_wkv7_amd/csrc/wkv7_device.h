@@ -188,13 +188,15 @@ __device__ __forceinline__ void wait_dma()
 }
 
 // One lane's 16 bytes from global memory to LDS at lds_wave_base + lane * 16
-// (the wave-uniform LDS byte address goes through M0).  Written as inline
+// (the LDS byte address, which must be the same in every lane of the wave,
+// goes through M0).  Written as inline
 // asm so the compiler does not treat later LDS reads as possibly reading
 // this copy: it would otherwise wait for every copy in flight before each
 // LDS read.  Completion is awaited explicitly with wait_dma().
 __device__ __forceinline__ void dma16(const void *gsrc, const float *lds_wave_base)
 {
-    const unsigned m0 = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) float *)lds_wave_base;
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)(const __attribute__((address_space(3))) float *)lds_wave_base);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(gsrc), "s"(m0)
