@@ -460,23 +460,31 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         auto solve_block = [&](auto tbc) {
             constexpr int tb = decltype(tbc)::value;
             const int slot = 10 + tix(tb, tb);
+            // every operand of the block first: the chain below then runs on
+            // registers only
+            float4 m[16];
+#pragma unroll
+            for (int tl = 1; tl < 16; ++tl) m[tl] = lds4(sP, slot * 256 + pt(tl, 0) + 4 * g);
+            float ao[tb > 0 ? tb : 1][4];
+#pragma unroll
+            for (int tp = 0; tp < tb; ++tp)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) ao[tp][s] = tA(10 + tix(tb, tp), s);
 #pragma unroll
             for (int tl = 15; tl >= 1; --tl) {
                 const float d = tl >= 12 ? bcast_group<3>(Rt[tb][tl & 3])
                               : tl >= 8 ? bcast_group<2>(Rt[tb][tl & 3])
                               : tl >= 4 ? bcast_group<1>(Rt[tb][tl & 3])
                                         : bcast_group<0>(Rt[tb][tl & 3]);
-                const float4 m = lds4(sP, slot * 256 + pt(tl, 0) + 4 * g);
-                Rt[tb][0] = fmaf(m.x, d, Rt[tb][0]);
-                Rt[tb][1] = fmaf(m.y, d, Rt[tb][1]);
-                Rt[tb][2] = fmaf(m.z, d, Rt[tb][2]);
-                Rt[tb][3] = fmaf(m.w, d, Rt[tb][3]);
+                Rt[tb][0] = fmaf(m[tl].x, d, Rt[tb][0]);
+                Rt[tb][1] = fmaf(m[tl].y, d, Rt[tb][1]);
+                Rt[tb][2] = fmaf(m[tl].z, d, Rt[tb][2]);
+                Rt[tb][3] = fmaf(m[tl].w, d, Rt[tb][3]);
             }
 #pragma unroll
             for (int tp = 0; tp < tb; ++tp)
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    Rt[tp] = mfma(tA(10 + tix(tb, tp), s), Rt[tb][s], Rt[tp]);
+                for (int s = 0; s < 4; ++s) Rt[tp] = mfma(ao[tp][s], Rt[tb][s], Rt[tp]);
         };
         solve_block(std::integral_constant<int, 3>{});
         solve_block(std::integral_constant<int, 2>{});
@@ -598,6 +606,7 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         value_pass(XK, sK);
         rows_times(XR, sDY, A, s0B);
         rows_times(XA, sD, A, s0B);
+        if (c > 0) issue_s0(c - 1);   // this chunk's S0 column is no longer needed
         __syncthreads();
         refresh();
 #pragma unroll
@@ -608,19 +617,37 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         __syncthreads();
         refresh();
 
-        // ---- pass 2: Grams dy sa^T, dsa sa^T; db bracket; bt terms of dr, da
-        gram(sDY, sD, sVS, none);
+        // ---- pass 2: Grams dy sa^T, dsa sa^T (dk written beside them); db
+        // bracket; bt terms of dr, da
+        const int64_t cb = vbase + t0 * stride;   // this chunk's outputs
+        float *odk = p.dk + cb, *odb = p.db + cb, *odr = p.dr + cb;
+        float *oda = p.da + cb, *odw = p.dw + cb, *odv = p.dv + cb;
+        gram(sDY, sD, sVS, [&](int k) {
+            if (k == 0) return;
+            const int tb = k - 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * tb + 4 * g + i;
+                const float gt = sG[A.col[i] + 1024 * tb];
+                if (t < Lc) odk[t * (int)stride + jw] = XK[tb][i] * __builtin_amdgcn_rcpf(gt);
+            }
+        });
         __syncthreads();
         refresh();
         value_pass(XB, sB);
         __syncthreads();
         refresh();
+        // next chunk: v (sa is done with) and, through registers, k and dy
+        if (c > 0) {
+#pragma unroll
+            for (int q = 0; q < 7; ++q) {
+                if (kDma && q == 5) issue_dma(c - 1, q);
+                else if (!kDma || q == 2 || q == 6) issue_regs(c - 1, q);
+            }
+        }
 
-        // ---- outputs dk, db, dr, da, dw (dw: prefix over steps of
+        // ---- outputs db, dr, da, dw (dw: prefix over steps of
         // k dk + b db - r dr - a da), beside the pass-3 Grams rb kt^T, ab kt^T
-        const int64_t cb = vbase + t0 * stride;   // this chunk's outputs
-        float *odk = p.dk + cb, *odb = p.db + cb, *odr = p.dr + cb;
-        float *oda = p.da + cb, *odw = p.dw + cb, *odv = p.dv + cb;
         float f[4][4], blk[16];
         auto outputs = [&](int k) {
             if (k == 0) {
@@ -655,7 +682,6 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                 const float wdw = (cj + ex) - adA;
                 if (t < Lc) {
                     const int off = t * (int)stride + jw;
-                    odk[off] = XK[tb][i] * inv;
                     odb[off] = XB[tb][i] * inv;
                     odr[off] = XR[tb][i] * gt;
                     oda[off] = XA[tb][i] * gp;
@@ -667,13 +693,12 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         gram(sR, sA, sK, outputs);
         __syncthreads();
         refresh();
-        if (c > 0) {
-#pragma unroll
-            for (int q = 0; q < 7; ++q) {
-                if (kDma && q != 2 && q != 6) issue_dma(c - 1, q);
-                else issue_regs(c - 1, q);
-            }
-            issue_s0(c - 1);
+        // next chunk: r, w, a, b straight into their (now free) arrays
+        if (kDma && c > 0) {
+            issue_dma(c - 1, 0);
+            issue_dma(c - 1, 1);
+            issue_dma(c - 1, 3);
+            issue_dma(c - 1, 4);
         }
         sched_fence();
 
