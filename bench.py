@@ -7,10 +7,13 @@ checkpoints every `chunk` steps) followed by the reverse scan that consumes
 those checkpoints and writes dr, dw, dk, dv, da, db and ds0.
 
 Prints ONE JSON line.  `value` is tokens (B*T) per second of fwd+bwd.
-`roofline` is for the dominant kernel (the reverse scan): its algorithmic
+`roofline` is for the dominant kernel (the reverse scan; at N = 64 and
+C = 64 its chunk form, whose contractions run on fp32 MFMA): its algorithmic
 fp32 flops per launch (26*N^2 per token-head) over its mean launch time,
 timed with HIP events on the stream it runs on, against the MI355X fp32
-vector peak.  `cpu_baseline` times the fp64 oracle on a bounded sample of
+peak (157.3 TFLOP/s, the same for dense fp32 MFMA and packed fp32 VALU).
+`fwd_only_tokens_per_s` times the forward alone without checkpoints
+(inference).  `cpu_baseline` times the fp64 oracle on a bounded sample of
 whole (b, h) recurrences of the same workload on the host's cores.
 """
 import argparse
@@ -173,6 +176,16 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
+    # forward alone, no checkpoints (inference), after the timed region
+    f0 = torch.cuda.Event(enable_timing=True)
+    f1 = torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(args.steps):
+        api.wkv7_forward(*(inp[n] for n in names), inp["s0"], chunk=C, want_ckpt=False,
+                         out=(y, sT, None), stream=stream)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    fwd_only_ms = f0.elapsed_time(f1) / args.steps
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     for n, x in list(grads.items()) + [("y", y), ("sT", sT)]:
@@ -180,6 +193,7 @@ def main():
             raise RuntimeError(f"non-finite values in {n}")
 
     fwd_flops, bwd_flops, fwd_bytes, bwd_bytes = algorithmic(wl)
+    chunked = N == 64 and C == 64   # the reverse scan's chunk form applies
     achieved = bwd_flops / (bwd_ms * 1e-3)
     traffic = measured_traffic(wl.name)
     t_roof = max((fwd_flops + bwd_flops) / PEAK_FP32_VALU, (fwd_bytes + bwd_bytes) / PEAK_HBM)
@@ -200,8 +214,8 @@ def main():
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "N": N, "chunk": C,
                    "input_dtype": wl.dtype, "s0": wl.has_s0, "dsT": wl.has_dsT},
         "roofline": {
-            "kernel": "wkv7_bwd_kernel",
-            "bound": "alu",
+            "kernel": "wkv7_bwdc_kernel" if chunked else "wkv7_bwd_kernel",
+            "bound": "mfma" if chunked else "alu",
             "achieved": achieved / 1e12,
             "peak": PEAK_FP32_VALU / 1e12,
             "unit": "TFLOP/s",
@@ -210,6 +224,7 @@ def main():
         },
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
+        "fwd_only_tokens_per_s": tokens / (fwd_only_ms * 1e-3),
         "fwd_bwd_roofline_frac": t_roof / (ms * 1e-3),
     }
     if args.copy_bytes > 0:
