@@ -203,7 +203,7 @@ __device__ __forceinline__ float bcast_group(float x)
 }
 
 template <typename TIn>
-__global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
+__global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 {
     // chunk vectors, [step][feature] swizzled: cumulative decay, rb, ab, kt,
     // bt, dsa (Hb until dsa is known), dy, and v (later sa)
@@ -212,46 +212,55 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
     // two Gram matrices (10 lower 16x16 tiles each)
     __shared__ __align__(16) float sP[20 * 256];
     __shared__ __align__(16) float sScan[4][256];
-    __shared__ __align__(16) float sCp[4][64];
+    __shared__ __align__(16) float sCp[8][64];
+    __shared__ __align__(16) float sCj[2][64];
+    // inverses of the four diagonal 16x16 blocks of the dsa system
+    __shared__ __align__(16) float sTT[4 * 256];
     __shared__ int sBad;
 
+    // 8 waves, two per SIMD: wave w works on feature columns 16 fb .. 16 fb + 15
+    // (fb = w % 4) of every output, for the time blocks {0, 3} (w < 4) or
+    // {1, 2} (w >= 4) of each chunk; the two waves on a SIMD share its matrix
+    // core, and each hides the other's waits.
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int fb = wave & 3, half = wave >> 2;
     const int64_t bh = blockIdx.x, T = p.T, H = p.H;
-    const int64_t bb_ = bh / H, hh = bh % H;
+    const int64_t bidx = bh / H, head = bh % H;
     const int64_t stride = H * 64;
-    const int64_t vbase = (bb_ * T * H + hh) * 64;
+    const int64_t vbase = (bidx * T * H + head) * 64;
     const int nck = p.nck;
     // every phase-2 tile of this lane is in feature column jw; state
-    // gradients are held as rows 16 g + s (s = 4 ib + i) of column jw
-    int l16 = lane & 15, g = lane >> 4, jw = wave * 16 + (lane & 15);
+    // gradients are held as rows 16 g + 4 ib + i of column jw, ib = 2 half + lb
+    int l16 = lane & 15, g = lane >> 4, jw = fb * 16 + (lane & 15), ltid = tid;
     // Makes the lane indices opaque again, so that the many LDS addresses
     // derived from them are recomputed where they are used instead of being
     // hoisted out of the chunk loop into (too many) registers.
     LaneAddr A;
     auto refresh = [&]() {
-        asm volatile("" : "+v"(l16), "+v"(g), "+v"(jw));
+        asm volatile("" : "+v"(l16), "+v"(g), "+v"(jw), "+v"(ltid));
         A = lane_addr(l16, g, jw);
     };
 
-    // dL/dS at the end of the chunk being processed (rows 16 g + s, column jw)
-    f4 Hc[4];
+    // dL/dS at the end of the chunk being processed: this wave's 32 rows of
+    // column jw
+    f4 Hc[2];
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+    for (int lb = 0; lb < 2; ++lb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            Hc[ib][i] = p.dsT ? p.dsT[bh * 4096 + (16 * g + 4 * ib + i) * 64 + jw] : 0.f;
+            Hc[lb][i] = p.dsT ? p.dsT[bh * 4096 + (16 * g + 4 * (2 * half + lb) + i) * 64 + jw] : 0.f;
     if (tid == 0) sBad = 0;
 
     // The inputs of a chunk (r, w, k, a, b, v, dy) and its checkpoint's
     // column jw (rows 16 g + s) are loaded one chunk ahead, during the
-    // previous chunk's last pass.  Every chunk but the last is full.  fp32
-    // r, w, a, b, v go straight to their LDS arrays (free by then); k and dy,
-    // and all bf16 inputs (widened on the way into LDS), go through
-    // registers: 4 float4 units per thread and input.
+    // previous chunk.  Every chunk but the last is full.  fp32 r, w, a, b, v
+    // go straight to their LDS arrays once those are free; k and dy, and all
+    // bf16 inputs (widened on the way into LDS), go through registers: 2
+    // float4 units per thread and input.
     using Raw = typename InQuad<TIn>::raw;
     constexpr bool kDma = std::is_same<TIn, float>::value;
-    Raw pre[7][4];
+    Raw pre[7][2];
     float s0B[16];
     const TIn *src_[7] = {p.r, p.w, p.k, p.a, p.b, p.v, p.dy};
     float *dst_[7] = {sR, sG, sK, sA, sB, sVS, sDY};
@@ -268,15 +277,15 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         const int64_t tt0 = (int64_t)cc * 64;
         const int Lcc = chunk_len(cc);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int u = tid + 256 * m, t = u >> 4, j4 = (u & 15) << 2;
+        for (int m = 0; m < 2; ++m) {
+            const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
             if (t < Lcc) pre[q][m] = InQuad<TIn>::load(src_[q] + vbase + (tt0 + t) * stride + j4);
         }
     };
     auto commit_regs = [&](int Lcc, int q) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int u = tid + 256 * m, t = u >> 4, j4 = (u & 15) << 2;
+        for (int m = 0; m < 2; ++m) {
+            const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
             const float d = q == 1 ? 1.f : 0.f;
             put4(dst_[q], sw(t, j4), t < Lcc ? InQuad<TIn>::f32(pre[q][m]) : make_float4(d, d, d, d));
         }
@@ -287,10 +296,10 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
     auto issue_dma = [&](int cc, int q) {
         const int64_t tt0 = (int64_t)cc * 64;
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) {
-            const int blk = wave + 4 * k4;
-            const int t = 4 * blk + (lane >> 4);
-            const int j4 = ((lane & 15) ^ (t & 15)) << 2;
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int blk = wave + 8 * k2;
+            const int t = 4 * blk + ((ltid & 63) >> 4);
+            const int j4 = ((ltid & 15) ^ (t & 15)) << 2;
             dma16(reinterpret_cast<const float *>(src_[q]) + vbase + (tt0 + t) * stride + j4,
                   dst_[q] + blk * 256);
         }
@@ -318,28 +327,28 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         __syncthreads();
         refresh();
 
-        // ---- cumulative decay, in place of w: 4 segments of 16 steps per column
+        // ---- cumulative decay, in place of w: 8 segments of 8 steps per column
         {
-            const int j = tid & 63, seg = tid >> 6;
+            const int j = ltid & 63, seg = ltid >> 6;
             float pr = 1.f;
 #pragma unroll
-            for (int u = 0; u < 16; ++u) pr *= sG[sw(seg * 16 + u, j)];
+            for (int u = 0; u < 8; ++u) pr *= sG[sw(seg * 8 + u, j)];
             sCp[seg][j] = pr;
         }
         __syncthreads();
         refresh();
         {
-            const int j = tid & 63, seg = tid >> 6;
-            float pre = 1.f;
-            for (int s2 = 0; s2 < seg; ++s2) pre *= sCp[s2][j];
+            const int j = ltid & 63, seg = ltid >> 6;
+            float pre_ = 1.f;
+            for (int s2 = 0; s2 < seg; ++s2) pre_ *= sCp[s2][j];
             bool ok = true;
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int o = sw(seg * 16 + u, j);
+            for (int u = 0; u < 8; ++u) {
+                const int o = sw(seg * 8 + u, j);
                 const float wv = sG[o];
-                pre *= wv;
-                ok = ok && wv >= kWMin && wv <= 1.f && pre >= kGMin;
-                sG[o] = pre;
+                pre_ *= wv;
+                ok = ok && wv >= kWMin && wv <= 1.f && pre_ >= kGMin;
+                sG[o] = pre_;
             }
             if (!ok) sBad = 1;   // every writer stores 1
         }
@@ -348,8 +357,8 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 
         // ---- rb = r g, ab = a g_prev, kt = k / g, bt = b / g; Hb = H g_63
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int u = tid + 256 * m, t = u >> 4, j4 = (u & 15) << 2;
+        for (int m = 0; m < 2; ++m) {
+            const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
             const int o = sw(t, j4);
             const float4 gm = lds4(sG, o);
             const float4 gp = t > 0 ? lds4(sG, sw(t - 1, j4)) : make_float4(1.f, 1.f, 1.f, 1.f);
@@ -363,24 +372,29 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             x = lds4(sB, o);
             put4(sB, o, make_float4(x.x * inv.x, x.y * inv.y, x.z * inv.z, x.w * inv.w));
         }
-        const float g63 = sG[sw(63, jw)];
-        float hB[16];   // Hb column jw, rows 16 g + s
+        {
+            const float g63 = sG[sw(63, jw)];
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            hB[s] = Hc[s >> 2][s & 3] * g63;
-            sD[sw(16 * g + s, jw)] = hB[s];
+            for (int lb = 0; lb < 2; ++lb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sD[sw(16 * g + 4 * (2 * half + lb) + i, jw)] = Hc[lb][i] * g63;
         }
         __syncthreads();
         refresh();
-        float hR[16];   // Hb row jw, columns 16 g + s
+        // Hb column jw (rows 16 g + s) and row jw (columns 16 g + s): the B
+        // operands of its phase-2 products
+        float hB[16], hR[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) hB[s] = sD[sw(16 * g + s, jw)];
         row16(sD, jw, 16 * g, hR);
 
         // Gram tiles: slot n < 10 holds rows of sX1 times rows of sY, slot
         // 10 + n rows of sX2 times rows of sY, for the lower block pair n
         // (rows a of the first factor, b of the second); the diagonal block
-        // keeps a >= b for sX1 and a > b for sX2.  Wave w takes n = w + 4k,
-        // k = 0..4, loading tile k + 1 while the MFMAs of tile k run; side(k)
-        // is independent work placed beside tile k's MFMAs.
+        // keeps a >= b for sX1 and a > b for sX2.  Wave w takes n = w, w + 8,
+        // w + 16 (< 20), loading tile k + 1 while the MFMAs of tile k run;
+        // side(k) is independent work placed beside tile k's MFMAs.
         auto gram_store = [&](int n, f4 acc) {
             const int pr = n < 10 ? n : n - 10;
             const bool diag = tab(pr) == tbb(pr);
@@ -406,24 +420,17 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                 gram_store(n, acc);
             };
             load(wave, xa, ya);
-            load(wave + 4, xb, yb);
+            load(wave + 8, xb, yb);
             side(0);
             run(wave, xa, ya);
             sched_fence();
-            load(wave + 8, xa, ya);
+            if (wave + 16 < 20) load(wave + 16, xa, ya);
             side(1);
-            run(wave + 4, xb, yb);
+            run(wave + 8, xb, yb);
             sched_fence();
-            load(wave + 12, xb, yb);
             side(2);
-            run(wave + 8, xa, ya);
+            if (wave + 16 < 20) run(wave + 16, xa, ya);
             sched_fence();
-            load(wave + 16, xa, ya);
-            side(3);
-            run(wave + 12, xb, yb);
-            sched_fence();
-            side(4);
-            run(wave + 16, xa, ya);
         };
         auto none = [](int) {};
         // Gram tile slot elements (4 g + s, l16) and (l16, 4 g + s), and
@@ -432,309 +439,374 @@ __global__ void __launch_bounds__(256) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         auto tAt = [&](int slot, int s) { return sP[slot * 256 + A.pb + s]; };
         auto colE = [&](const float *arr, int ub, int s) { return arr[A.col[s] + 1024 * ub]; };
 
-        // ---- dsa for the chunk: dsa_t = rhs_t + sum_{u>t} dsa_u (ab_u . bt_t),
-        // rhs_t = Hb bt_t + sum_{u>=t} dy_u (rb_u . bt_t).  Rows i = jw,
-        // steps t = 16 tb + 4 g + i of f4 Rt[tb].
-        gram(sR, sA, sB, none);
-        __syncthreads();
-        refresh();
-        f4 Rt[4];
+        auto body = [&](auto hc) {
+            constexpr int HF = decltype(hc)::value;
+            constexpr int TB[2] = {HF ? 1 : 0, HF ? 2 : 3};   // this wave's time blocks
+            // X[lt] += rows of sX in time block TB[lt] times bv (K = 64)
+            auto rows2 = [&](f4 (&X)[2], const float *sX, const float (&bv)[16]) {
+                pipelined<2, 16>([&](int lt, float (&b)[16]) { rowl(sX, A, TB[lt], b); },
+                                 [&](int lt, const float (&b)[16]) {
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) Rt[tb] = f4{0.f, 0.f, 0.f, 0.f};
-        rows_times(Rt, sB, A, hR);
-        pipelined<16, 5>(
-            [&](int k, float (&b)[5]) {
-                const int ub = k >> 2, s = k & 3;
-                b[0] = colE(sDY, ub, s);
+                                     for (int s = 0; s < 16; ++s) X[lt] = mfma(b[s], bv[s], X[lt]);
+                                 });
+            };
+            f4 XR[2], XA[2], XK[2], XB[2], XV[2];
 #pragma unroll
-                for (int tb = 0; tb <= ub; ++tb) b[1 + tb] = tA(tix(ub, tb), s);
-            },
-            [&](int k, const float (&b)[5]) {
-                const int ub = k >> 2;
-#pragma unroll
-                for (int tb = 0; tb <= ub; ++tb) Rt[tb] = mfma(b[1 + tb], b[0], Rt[tb]);
-            });
-        // blocked back substitution: the diagonal block step by step (each
-        // finished dsa broadcast to the row groups), then its contribution to
-        // the earlier blocks on MFMA
-        auto solve_block = [&](auto tbc) {
-            constexpr int tb = decltype(tbc)::value;
-            const int slot = 10 + tix(tb, tb);
-            // every operand of the block first: the chain below then runs on
-            // registers only
-            float4 m[16];
-#pragma unroll
-            for (int tl = 1; tl < 16; ++tl) m[tl] = lds4(sP, slot * 256 + pt(tl, 0) + 4 * g);
-            float ao[tb > 0 ? tb : 1][4];
-#pragma unroll
-            for (int tp = 0; tp < tb; ++tp)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) ao[tp][s] = tA(10 + tix(tb, tp), s);
-#pragma unroll
-            for (int tl = 15; tl >= 1; --tl) {
-                const float d = tl >= 12 ? bcast_group<3>(Rt[tb][tl & 3])
-                              : tl >= 8 ? bcast_group<2>(Rt[tb][tl & 3])
-                              : tl >= 4 ? bcast_group<1>(Rt[tb][tl & 3])
-                                        : bcast_group<0>(Rt[tb][tl & 3]);
-                Rt[tb][0] = fmaf(m[tl].x, d, Rt[tb][0]);
-                Rt[tb][1] = fmaf(m[tl].y, d, Rt[tb][1]);
-                Rt[tb][2] = fmaf(m[tl].z, d, Rt[tb][2]);
-                Rt[tb][3] = fmaf(m[tl].w, d, Rt[tb][3]);
+            for (int lt = 0; lt < 2; ++lt) {
+                XR[lt] = f4{0.f, 0.f, 0.f, 0.f};
+                XA[lt] = XR[lt];
+                XK[lt] = XR[lt];
+                XB[lt] = XR[lt];
+                XV[lt] = XR[lt];
             }
+            // the state gradient entering the chunk, this wave's rows: Hb,
+            // then + sum_u dy_u rb_u^T (now) and dsa_u ab_u^T (once dsa is
+            // known).  MFMA row m = l16 stands for row 16 (m / 4) + 4 ib + m % 4.
+            f4 Hn[2];
 #pragma unroll
-            for (int tp = 0; tp < tb; ++tp)
+            for (int lb = 0; lb < 2; ++lb)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) Rt[tp] = mfma(ao[tp][s], Rt[tb][s], Rt[tp]);
-        };
-        solve_block(std::integral_constant<int, 3>{});
-        solve_block(std::integral_constant<int, 2>{});
-        solve_block(std::integral_constant<int, 1>{});
-        solve_block(std::integral_constant<int, 0>{});
+                for (int i = 0; i < 4; ++i) Hn[lb][i] = hB[4 * (2 * HF + lb) + i];
+            auto hprev_part = [&](const float *sX, const float *sF) {
+                pipelined<16, 6>(
+                    [&](int k, float (&b)[6]) {
+                        const int ub = k >> 2, s = k & 3;
+                        b[0] = colE(sF, ub, s);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+                        for (int lb = 0; lb < 2; ++lb)
+                            b[1 + lb] = sX[A.hrow + 1024 * ub + 64 * s + 4 * ((2 * HF + lb) ^ s)];
+                    },
+                    [&](int k, const float (&b)[6]) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tb + 4 * g + i;
-                sD[A.col[i] + 1024 * tb] = t < Lc ? Rt[tb][i] : 0.f;
+                        for (int lb = 0; lb < 2; ++lb) Hn[lb] = mfma(b[1 + lb], b[0], Hn[lb]);
+                    });
+            };
+            // the products that do not need dsa
+            auto pd_xk = [&]() { rows2(XK, sVS, hB); };    // Hb^T v_t
+            auto pd_xr = [&]() { rows2(XR, sDY, s0B); };   // S0^T dy_t
+            auto pd_xv = [&]() { rows2(XV, sK, hR); };     // Hb kt_t
+            auto pd_h = [&]() { hprev_part(sDY, sR); };
+
+            // ---- dsa for the chunk: dsa_t = rhs_t + sum_{u>t} dsa_u (ab_u . bt_t),
+            // rhs_t = Hb bt_t + sum_{u>=t} dy_u (rb_u . bt_t).  Rows i = jw,
+            // steps t = 16 tb + 4 g + i of f4 Rt[tb].  Blocked back
+            // substitution: the inverse of each 16x16 diagonal block,
+            // T_b = (I - N_b)^-1 with N_b[t][u] = ab_u . bt_t (u > t, both in
+            // block b), depends only on ab and bt, so the second-half wave fb
+            // forms T_fb (the step-by-step substitution with the 16 unit
+            // vectors as right-hand sides, one per lane column, each finished
+            // value broadcast across the row groups) while the first-half
+            // waves form rhs; the first half then applies T_3, updates the
+            // earlier blocks, applies T_2, ... on MFMA, while the second half
+            // runs its dsa-free products on the same matrix cores.
+            gram(sR, sA, sB, none);
+            __syncthreads();
+            refresh();
+            f4 Rt[4];
+            if constexpr (HF == 0) {
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) Rt[tb] = f4{0.f, 0.f, 0.f, 0.f};
+                rows_times(Rt, sB, A, hR);
+                pipelined<16, 5>(
+                    [&](int k, float (&b)[5]) {
+                        const int ub = k >> 2, s = k & 3;
+                        b[0] = colE(sDY, ub, s);
+#pragma unroll
+                        for (int tb = 0; tb <= ub; ++tb) b[1 + tb] = tA(tix(ub, tb), s);
+                    },
+                    [&](int k, const float (&b)[5]) {
+                        const int ub = k >> 2;
+#pragma unroll
+                        for (int tb = 0; tb <= ub; ++tb) Rt[tb] = mfma(b[1 + tb], b[0], Rt[tb]);
+                    });
+            } else {
+                const int slot = 10 + tix(fb, fb);
+                f4 X;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) X[i] = (4 * g + i == l16) ? 1.f : 0.f;
+                // the coefficient rows are read four steps ahead of the chain
+                float4 m[4];
+                auto mrow = [&](int tl) { return lds4(sP, slot * 256 + pt(tl, 0) + 4 * g); };
+#pragma unroll
+                for (int tl = 15; tl >= 12; --tl) m[tl & 3] = mrow(tl);
+#pragma unroll
+                for (int tl = 15; tl >= 1; --tl) {
+                    const float d = tl >= 12 ? bcast_group<3>(X[tl & 3])
+                                  : tl >= 8 ? bcast_group<2>(X[tl & 3])
+                                  : tl >= 4 ? bcast_group<1>(X[tl & 3])
+                                            : bcast_group<0>(X[tl & 3]);
+                    const float4 mm = m[tl & 3];
+                    if (tl >= 5) m[tl & 3] = mrow(tl - 4);
+                    X[0] = fmaf(mm.x, d, X[0]);
+                    X[1] = fmaf(mm.y, d, X[1]);
+                    X[2] = fmaf(mm.z, d, X[2]);
+                    X[3] = fmaf(mm.w, d, X[3]);
+                }
+                // T_fb[t][c] at tile position (t, c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sTT[fb * 256 + A.pa[i]] = X[i];
+                pd_xk();
+                pd_xv();
             }
-        __syncthreads();
-        refresh();
-
-        // ---- dL/dS before the chunk: Hb + sum_u dy_u rb_u^T + dsa_u ab_u^T
-        // (rows 16 g + s: the MFMA row m = l16 stands for row 16 (m / 4) + 4 ib + m % 4)
-        {
+            __syncthreads();
+            refresh();
+            if constexpr (HF == 0) {
+                auto apply_block = [&](auto tbc) {
+                    constexpr int tb = decltype(tbc)::value;
+                    f4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ib = 0; ib < 4; ++ib)
+                    for (int s = 0; s < 4; ++s) x = mfma(sTT[tb * 256 + A.pb + s], Rt[tb][s], x);
+                    Rt[tb] = x;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Hc[ib][i] = hB[4 * ib + i];
-            pipelined<16, 10>(
-                [&](int k, float (&b)[10]) {
-                    const int ub = k >> 2, s = k & 3;
-                    b[0] = colE(sR, ub, s);
-                    b[1] = colE(sA, ub, s);
+                    for (int tp = 0; tp < tb; ++tp)
 #pragma unroll
-                    for (int ib = 0; ib < 4; ++ib) {
-                        const int o = A.hrow + 1024 * ub + 64 * s + 4 * (ib ^ s);
-                        b[2 + 2 * ib] = sDY[o];
-                        b[3 + 2 * ib] = sD[o];
-                    }
-                },
-                [&](int k, const float (&b)[10]) {
+                        for (int s = 0; s < 4; ++s) Rt[tp] = mfma(tA(10 + tix(tb, tp), s), Rt[tb][s], Rt[tp]);
+                };
+                // the dsa-free products fill the gaps of the dependent chain
+                apply_block(std::integral_constant<int, 3>{});
+                pd_xk();
+                apply_block(std::integral_constant<int, 2>{});
+                pd_xr();
+                apply_block(std::integral_constant<int, 1>{});
+                pd_xv();
+                apply_block(std::integral_constant<int, 0>{});
+                pd_h();
 #pragma unroll
-                    for (int ib = 0; ib < 4; ++ib) {
-                        Hc[ib] = mfma(b[2 + 2 * ib], b[0], Hc[ib]);
-                        Hc[ib] = mfma(b[3 + 2 * ib], b[1], Hc[ib]);
-                    }
-                });
-        }
-        // c_j = sum_i (dL/dS0)[i][j] S0[i][j]; ds0 after the first chunk
-        float cj = 0.f;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) cj = fmaf(Hc[s >> 2][s & 3], s0B[s], cj);
-        cj = swap_add16(cj, cj);
-        cj = swap_add32(cj, cj);
-        if (c == 0 && p.ds0) {
-#pragma unroll
-            for (int s = 0; s < 16; ++s) p.ds0[bh * 4096 + (16 * g + s) * 64 + jw] = Hc[s >> 2][s & 3];
-        }
-
-        // sa for the second pass, loaded while the first one runs
-        float4 saR[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int u = tid + 256 * m, t = u >> 4, j4 = (u & 15) << 2;
-            saR[m] = t < Lc ? *reinterpret_cast<const float4 *>(p.sa + vbase + (t0 + t) * stride + j4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-
-        f4 XR[4], XA[4], XK[4], XB[4];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            XR[tb] = f4{0.f, 0.f, 0.f, 0.f};
-            XA[tb] = XR[tb];
-            XK[tb] = XR[tb];
-            XB[tb] = XR[tb];
-        }
-        // One pass over the Grams of the value-side vectors in sVS (v, then
-        // sa): X (dk, then db bracket) gets Hb^T x_t + sum_{u>=t} rb_u (dy_u.x_t)
-        // + sum_{u>t} ab_u (dsa_u.x_t); the dr, da brackets get
-        // sum_{u<=t} f_u (x_u.dy_t) and sum_{u<t} f_u (x_u.dsa_t) with the
-        // key-side vector sF (kt, then bt).
-        auto value_pass = [&](f4 (&X)[4], const float *sF) {
-            rows_times(X, sVS, A, hB);
-            // per group (ub, s): br, ba, bf, then the A operands in MFMA order
-            pipelined<16, 13>(
-                [&](int k, float (&b)[13]) {
-                    const int ub = k >> 2, s = k & 3;
-                    b[0] = colE(sR, ub, s);
-                    b[1] = colE(sA, ub, s);
-                    b[2] = colE(sF, ub, s);
-                    int n = 3;
-#pragma unroll
-                    for (int tb = 0; tb <= ub; ++tb) {
-                        b[n++] = tA(tix(ub, tb), s);
-                        b[n++] = tA(10 + tix(ub, tb), s);
-                    }
-#pragma unroll
-                    for (int tb = ub; tb < 4; ++tb) {
-                        b[n++] = tAt(tix(tb, ub), s);
-                        b[n++] = tAt(10 + tix(tb, ub), s);
-                    }
-                },
-                [&](int k, const float (&b)[13]) {
-                    const int ub = k >> 2;
-                    int n = 3;
-#pragma unroll
-                    for (int tb = 0; tb <= ub; ++tb) {
-                        X[tb] = mfma(b[n], b[0], X[tb]);
-                        X[tb] = mfma(b[n + 1], b[1], X[tb]);
-                        n += 2;
-                    }
-#pragma unroll
-                    for (int tb = ub; tb < 4; ++tb) {
-                        XR[tb] = mfma(b[n], b[2], XR[tb]);
-                        XA[tb] = mfma(b[n + 1], b[2], XA[tb]);
-                        n += 2;
-                    }
-                });
-        };
-
-        // ---- pass 1: Grams dy v^T, dsa v^T; dk bracket; S0 and kt terms of dr, da
-        gram(sDY, sD, sVS, none);
-        __syncthreads();
-        refresh();
-        value_pass(XK, sK);
-        rows_times(XR, sDY, A, s0B);
-        rows_times(XA, sD, A, s0B);
-        if (c > 0) issue_s0(c - 1);   // this chunk's S0 column is no longer needed
-        __syncthreads();
-        refresh();
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int u = tid + 256 * m, t = u >> 4, j4 = (u & 15) << 2;
-            put4(sVS, sw(t, j4), saR[m]);
-        }
-        __syncthreads();
-        refresh();
-
-        // ---- pass 2: Grams dy sa^T, dsa sa^T (dk written beside them); db
-        // bracket; bt terms of dr, da
-        const int64_t cb = vbase + t0 * stride;   // this chunk's outputs
-        float *odk = p.dk + cb, *odb = p.db + cb, *odr = p.dr + cb;
-        float *oda = p.da + cb, *odw = p.dw + cb, *odv = p.dv + cb;
-        gram(sDY, sD, sVS, [&](int k) {
-            if (k == 0) return;
-            const int tb = k - 1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tb + 4 * g + i;
-                const float gt = sG[A.col[i] + 1024 * tb];
-                if (t < Lc) odk[t * (int)stride + jw] = XK[tb][i] * __builtin_amdgcn_rcpf(gt);
-            }
-        });
-        __syncthreads();
-        refresh();
-        value_pass(XB, sB);
-        __syncthreads();
-        refresh();
-        // next chunk: v (sa is done with) and, through registers, k and dy
-        if (c > 0) {
-#pragma unroll
-            for (int q = 0; q < 7; ++q) {
-                if (kDma && q == 5) issue_dma(c - 1, q);
-                else if (!kDma || q == 2 || q == 6) issue_regs(c - 1, q);
-            }
-        }
-
-        // ---- outputs db, dr, da, dw (dw: prefix over steps of
-        // k dk + b db - r dr - a da), beside the pass-3 Grams rb kt^T, ab kt^T
-        float f[4][4], blk[16];
-        auto outputs = [&](int k) {
-            if (k == 0) {
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
+                for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int o = A.col[i] + 1024 * tb;
-                        f[tb][i] = sK[o] * XK[tb][i] + sB[o] * XB[tb][i] - sR[o] * XR[tb][i] -
-                                   sA[o] * XA[tb][i];
+                        const int t = 16 * tb + 4 * g + i;
+                        sD[A.col[i] + 1024 * tb] = t < Lc ? Rt[tb][i] : 0.f;
                     }
-                    sScan[wave][(4 * tb + g) * 16 + l16] = ((f[tb][0] + f[tb][1]) + f[tb][2]) + f[tb][3];
-                }
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-                for (int q = 0; q < 16; ++q) blk[q] = sScan[wave][q * 16 + l16];
-                return;
+            } else {
+                pd_xr();
+                pd_h();
             }
-            const int tb = k - 1;
-            float ex = 0.f;
+            __syncthreads();
+            refresh();
+            hprev_part(sD, sA);
+            rows2(XA, sD, s0B);    // S0^T dsa_t
+            // c_j = sum_i (dL/dS0)[i][j] S0[i][j]: this wave's rows; ds0 after
+            // the first chunk
+            {
+                float cp = 0.f;
 #pragma unroll
-            for (int q = 0; q < 16; ++q)
-                if (q < 4 * tb + g) ex += blk[q];
+                for (int lb = 0; lb < 2; ++lb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tb + 4 * g + i;
-                const int o = A.col[i] + 1024 * tb;
-                const float gt = sG[o];
-                const float gp = i > 0 ? sG[A.col[i - 1] + 1024 * tb] : t > 0 ? sG[sw(t - 1, jw)] : 1.f;
-                const float inv = __builtin_amdgcn_rcpf(gt);
-                const float adA = sA[o] * XA[tb][i];
-                const float wdw = (cj + ex) - adA;
-                if (t < Lc) {
-                    const int off = t * (int)stride + jw;
-                    odb[off] = XB[tb][i] * inv;
-                    odr[off] = XR[tb][i] * gt;
-                    oda[off] = XA[tb][i] * gp;
-                    odw[off] = wdw * gp * inv;
+                    for (int i = 0; i < 4; ++i) cp = fmaf(Hn[lb][i], s0B[4 * (2 * HF + lb) + i], cp);
+                cp = swap_add16(cp, cp);
+                cp = swap_add32(cp, cp);
+                if (g == 0) sCj[HF][jw] = cp;
+                if (c == 0 && p.ds0) {
+#pragma unroll
+                    for (int lb = 0; lb < 2; ++lb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            p.ds0[bh * 4096 + (16 * g + 4 * (2 * HF + lb) + i) * 64 + jw] = Hn[lb][i];
                 }
-                ex += f[tb][i];
+#pragma unroll
+                for (int lb = 0; lb < 2; ++lb) Hc[lb] = Hn[lb];
             }
-        };
-        gram(sR, sA, sK, outputs);
-        __syncthreads();
-        refresh();
-        // next chunk: r, w, a, b straight into their (now free) arrays
-        if (kDma && c > 0) {
-            issue_dma(c - 1, 0);
-            issue_dma(c - 1, 1);
-            issue_dma(c - 1, 3);
-            issue_dma(c - 1, 4);
-        }
-        sched_fence();
+            if (c > 0) issue_s0(c - 1);   // this chunk's S0 column is no longer needed
+            // sa for the second pass, loaded while the first one runs
+            float4 saR[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
+                saR[m] = t < Lc ? *reinterpret_cast<const float4 *>(p.sa + vbase + (t0 + t) * stride + j4)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
 
-        // ---- dv = Hb kt_t + sum_{u>=t} dy_u (rb_u . kt_t) + sum_{u>t} dsa_u (ab_u . kt_t)
-        f4 XV[4];
+            // One pass over the Grams of the value-side vectors in sVS (v,
+            // then sa): X (dk, then db bracket) gets sum_{u>=t} rb_u (dy_u.x_t)
+            // + sum_{u>t} ab_u (dsa_u.x_t); the dr, da brackets get
+            // sum_{u<=t} f_u (x_u.dy_t) and sum_{u<t} f_u (x_u.dsa_t) with the
+            // key-side vector sF (kt, then bt).  Groups (ub, s); per group the
+            // operands br, ba, bf, then the A operands in MFMA order.
+            auto value_terms = [&](f4 (&X)[2], const float *sF) {
+                pipelined<16, 11>(
+                    [&](int k, float (&b)[11]) {
+                        const int ub = k >> 2, s = k & 3;
+                        b[0] = colE(sR, ub, s);
+                        b[1] = colE(sA, ub, s);
+                        b[2] = colE(sF, ub, s);
+                        int n = 3;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) XV[tb] = f4{0.f, 0.f, 0.f, 0.f};
-        rows_times(XV, sK, A, hR);
-        pipelined<16, 10>(
-            [&](int k, float (&b)[10]) {
-                const int ub = k >> 2, s = k & 3;
-                b[0] = colE(sDY, ub, s);
-                b[1] = colE(sD, ub, s);
+                        for (int lt = 0; lt < 2; ++lt)
+                            if (TB[lt] <= ub) {
+                                b[n++] = tA(tix(ub, TB[lt]), s);
+                                b[n++] = tA(10 + tix(ub, TB[lt]), s);
+                            }
 #pragma unroll
-                for (int tb = 0; tb <= ub; ++tb) {
-                    b[2 + 2 * tb] = tA(tix(ub, tb), s);
-                    b[3 + 2 * tb] = tA(10 + tix(ub, tb), s);
-                }
-            },
-            [&](int k, const float (&b)[10]) {
-                const int ub = k >> 2;
+                        for (int lt = 0; lt < 2; ++lt)
+                            if (TB[lt] >= ub) {
+                                b[n++] = tAt(tix(TB[lt], ub), s);
+                                b[n++] = tAt(10 + tix(TB[lt], ub), s);
+                            }
+                    },
+                    [&](int k, const float (&b)[11]) {
+                        const int ub = k >> 2;
+                        int n = 3;
 #pragma unroll
-                for (int tb = 0; tb <= ub; ++tb) {
-                    XV[tb] = mfma(b[2 + 2 * tb], b[0], XV[tb]);
-                    XV[tb] = mfma(b[3 + 2 * tb], b[1], XV[tb]);
+                        for (int lt = 0; lt < 2; ++lt)
+                            if (TB[lt] <= ub) {
+                                X[lt] = mfma(b[n], b[0], X[lt]);
+                                X[lt] = mfma(b[n + 1], b[1], X[lt]);
+                                n += 2;
+                            }
+#pragma unroll
+                        for (int lt = 0; lt < 2; ++lt)
+                            if (TB[lt] >= ub) {
+                                XR[lt] = mfma(b[n], b[2], XR[lt]);
+                                XA[lt] = mfma(b[n + 1], b[2], XA[lt]);
+                                n += 2;
+                            }
+                    });
+            };
+
+            // ---- pass 1: Grams dy v^T, dsa v^T; dk bracket; kt terms of dr, da
+            gram(sDY, sD, sVS, none);
+            __syncthreads();
+            refresh();
+            value_terms(XK, sK);
+            __syncthreads();
+            refresh();
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
+                put4(sVS, sw(t, j4), saR[m]);
+            }
+            __syncthreads();
+            refresh();
+
+            // ---- pass 2: Grams dy sa^T, dsa sa^T (dk written beside them);
+            // db bracket; bt terms of dr, da; then the per-block sums of
+            // k dk + b db - r dr - a da for the dw prefix
+            const int64_t cb = vbase + t0 * stride;   // this chunk's outputs
+            float *odk = p.dk + cb, *odb = p.db + cb, *odr = p.dr + cb;
+            float *oda = p.da + cb, *odw = p.dw + cb, *odv = p.dv + cb;
+            gram(sDY, sD, sVS, [&](int k) {
+                if (k > 1) return;
+                const int tb = TB[k];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * tb + 4 * g + i;
+                    const float gt = sG[A.col[i] + 1024 * tb];
+                    if (t < Lc) odk[t * (int)stride + jw] = XK[k][i] * __builtin_amdgcn_rcpf(gt);
                 }
             });
+            __syncthreads();
+            refresh();
+            rows2(XB, sVS, hB);    // Hb^T sa_t
+            value_terms(XB, sB);
+            float f[2][4];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+            for (int lt = 0; lt < 2; ++lt) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tb + 4 * g + i;
-                if (t < Lc) odv[t * (int)stride + jw] = XV[tb][i];
+                for (int i = 0; i < 4; ++i) {
+                    const int o = A.col[i] + 1024 * TB[lt];
+                    f[lt][i] = sK[o] * XK[lt][i] + sB[o] * XB[lt][i] - sR[o] * XR[lt][i] -
+                               sA[o] * XA[lt][i];
+                }
+                sScan[fb][(4 * TB[lt] + g) * 16 + l16] = ((f[lt][0] + f[lt][1]) + f[lt][2]) + f[lt][3];
             }
-        __syncthreads();
-        refresh();
+            __syncthreads();
+            refresh();
+            // next chunk: v (sa is done with) and, through registers, k and dy
+            if (c > 0) {
+#pragma unroll
+                for (int q = 0; q < 7; ++q) {
+                    if (kDma && q == 5) issue_dma(c - 1, q);
+                    else if (!kDma || q == 2 || q == 6) issue_regs(c - 1, q);
+                }
+            }
+
+            // ---- outputs db, dr, da, dw (dw: prefix over steps of
+            // k dk + b db - r dr - a da), beside the pass-3 Grams rb kt^T, ab kt^T
+            float pre16[17];
+            auto outputs = [&](int k) {
+                if (k == 0) {
+                    // exclusive prefix of the 16 block sums of column jw (fixed order)
+                    pre16[0] = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) pre16[q + 1] = pre16[q] + sScan[fb][q * 16 + l16];
+                    return;
+                }
+                if (k > 2) return;
+                const int lt = k - 1, tb = TB[lt];
+                const float cj = sCj[0][jw] + sCj[1][jw];
+                const int q0 = 4 * tb + g;
+                float ex = g == 0 ? pre16[4 * tb] : g == 1 ? pre16[4 * tb + 1]
+                         : g == 2 ? pre16[4 * tb + 2] : pre16[4 * tb + 3];
+                (void)q0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * tb + 4 * g + i;
+                    const int o = A.col[i] + 1024 * tb;
+                    const float gt = sG[o];
+                    const float gp = i > 0 ? sG[A.col[i - 1] + 1024 * tb] : t > 0 ? sG[sw(t - 1, jw)] : 1.f;
+                    const float inv = __builtin_amdgcn_rcpf(gt);
+                    const float adA = sA[o] * XA[lt][i];
+                    const float wdw = (cj + ex) - adA;
+                    if (t < Lc) {
+                        const int off = t * (int)stride + jw;
+                        odb[off] = XB[lt][i] * inv;
+                        odr[off] = XR[lt][i] * gt;
+                        oda[off] = XA[lt][i] * gp;
+                        odw[off] = wdw * gp * inv;
+                    }
+                    ex += f[lt][i];
+                }
+            };
+            gram(sR, sA, sK, outputs);
+            __syncthreads();
+            refresh();
+            // next chunk: r, w, a, b straight into their (now free) arrays
+            if (kDma && c > 0) {
+                issue_dma(c - 1, 0);
+                issue_dma(c - 1, 1);
+                issue_dma(c - 1, 3);
+                issue_dma(c - 1, 4);
+            }
+            sched_fence();
+
+            // ---- dv = Hb kt_t + sum_{u>=t} dy_u (rb_u . kt_t) + sum_{u>t} dsa_u (ab_u . kt_t)
+            pipelined<16, 6>(
+                [&](int k, float (&b)[6]) {
+                    const int ub = k >> 2, s = k & 3;
+                    b[0] = colE(sDY, ub, s);
+                    b[1] = colE(sD, ub, s);
+                    int n = 2;
+#pragma unroll
+                    for (int lt = 0; lt < 2; ++lt)
+                        if (TB[lt] <= ub) {
+                            b[n++] = tA(tix(ub, TB[lt]), s);
+                            b[n++] = tA(10 + tix(ub, TB[lt]), s);
+                        }
+                },
+                [&](int k, const float (&b)[6]) {
+                    const int ub = k >> 2;
+                    int n = 2;
+#pragma unroll
+                    for (int lt = 0; lt < 2; ++lt)
+                        if (TB[lt] <= ub) {
+                            XV[lt] = mfma(b[n], b[0], XV[lt]);
+                            XV[lt] = mfma(b[n + 1], b[1], XV[lt]);
+                            n += 2;
+                        }
+                });
+#pragma unroll
+            for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * TB[lt] + 4 * g + i;
+                    if (t < Lc) odv[t * (int)stride + jw] = XV[lt][i];
+                }
+            __syncthreads();
+            refresh();
+        };
+        if (half == 0) body(std::integral_constant<int, 0>{});
+        else body(std::integral_constant<int, 1>{});
     }
 
     __syncthreads();
@@ -766,7 +838,7 @@ hipError_t launch_bwdc_t(const BwdLaunch &a, int *flags, hipStream_t stream)
     p.T = a.T;
     p.H = a.H;
     p.nck = (int)((a.T + 63) / 64);
-    hipLaunchKernelGGL((wkv7_bwdc_kernel<TIn>), dim3((unsigned)(a.B * a.H)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((wkv7_bwdc_kernel<TIn>), dim3((unsigned)(a.B * a.H)), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
