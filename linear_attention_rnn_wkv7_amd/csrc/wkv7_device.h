@@ -203,6 +203,23 @@ __device__ __forceinline__ void dma16(const void *gsrc, const float *lds_wave_ba
                  : "memory", "m0");
 }
 
+// The same with the global address split into a wave-uniform base (SGPRs)
+// and a 32-bit per-lane byte offset, and the LDS byte address given as a
+// wave-uniform value.
+__device__ __forceinline__ void dma16_split(const void *gbase, unsigned lane_off, unsigned lds_addr)
+{
+    // (readfirstlane returns int: widen through uint32_t, not by sign)
+    const uint64_t b = (uint64_t)(uintptr_t)gbase;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(lane_off), "s"(bs), "s"(m0)
+                 : "memory", "m0");
+}
+
 template <int NV, int TB, int N, int NTHREADS>
 struct DmaStager {
     using Geo = Stager<float, NV, TB, N, NTHREADS>;

@@ -280,9 +280,11 @@ hipError_t launch_fwd_t(const FwdLaunch &a, hipStream_t stream)
 
 hipError_t launch_forward(const FwdLaunch &a, hipStream_t stream)
 {
-    if (a.N == 64)
+    if (a.N == 64) {
+        if (forward_chunked_supported(a)) return launch_forward_chunked(a, stream);
         return a.dtype == 0 ? launch_fwd_t<64, float>(a, stream)
                             : launch_fwd_t<64, uint16_t>(a, stream);
+    }
     return a.dtype == 0 ? launch_fwd_t<16, float>(a, stream)
                         : launch_fwd_t<16, uint16_t>(a, stream);
 }

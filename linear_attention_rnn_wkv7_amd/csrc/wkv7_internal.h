@@ -40,6 +40,10 @@ struct BwdLaunch {
 size_t sub_bytes(int64_t B, int64_t H, int64_t N, int chunk);
 
 hipError_t launch_forward(const FwdLaunch &a, hipStream_t stream);
+// The forward for N = 64 on a scan plus matrix-core helper waves
+// (wkv7_fwdc.hip); it needs checkpoints on 32-step block starts.
+bool forward_chunked_supported(const FwdLaunch &a);
+hipError_t launch_forward_chunked(const FwdLaunch &a, hipStream_t stream);
 // Reverse scan: the chunk form where it applies (and algo allows), then the
 // step-by-step scan for every head the chunk form flagged (or all heads).
 hipError_t launch_backward(const BwdLaunch &a, hipStream_t stream);

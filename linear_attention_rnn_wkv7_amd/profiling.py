@@ -20,6 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ("linear_attention_rnn_wkv7_amd/csrc/wkv7_bwd.hip",
                   "linear_attention_rnn_wkv7_amd/csrc/wkv7_bwdc.hip",
                   "linear_attention_rnn_wkv7_amd/csrc/wkv7_fwd.hip",
+                  "linear_attention_rnn_wkv7_amd/csrc/wkv7_fwdc.hip",
                   "linear_attention_rnn_wkv7_amd/csrc/wkv7_device.h")
 
 
