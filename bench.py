@@ -47,10 +47,10 @@ def algorithmic(wl):
     return fwd_flops, bwd_flops, fwd_bytes, bwd_bytes
 
 
-def measured_traffic(workload):
-    """HBM bytes per backward launch from committed rocprofv3 counter runs,
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs,
     or None when absent or taken on a different kernel source."""
-    path = os.path.join(PROFILES, f"wkv7_bwd_{workload}_traffic.json")
+    path = os.path.join(PROFILES, f"{kernel.replace('_kernel', '')}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -195,7 +195,8 @@ def main():
     fwd_flops, bwd_flops, fwd_bytes, bwd_bytes = algorithmic(wl)
     chunked = N == 64 and C == 64   # the reverse scan's chunk form applies
     achieved = bwd_flops / (bwd_ms * 1e-3)
-    traffic = measured_traffic(wl.name)
+    kernel = "wkv7_bwdc_kernel" if chunked else "wkv7_bwd_kernel"
+    traffic = measured_traffic(kernel, wl.name)
     t_roof = max((fwd_flops + bwd_flops) / PEAK_FP32_VALU, (fwd_bytes + bwd_bytes) / PEAK_HBM)
     tokens = B * T
     rec = {
@@ -214,7 +215,7 @@ def main():
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "N": N, "chunk": C,
                    "input_dtype": wl.dtype, "s0": wl.has_s0, "dsT": wl.has_dsT},
         "roofline": {
-            "kernel": "wkv7_bwdc_kernel" if chunked else "wkv7_bwd_kernel",
+            "kernel": kernel,
             "bound": "mfma" if chunked else "alu",
             "achieved": achieved / 1e12,
             "peak": PEAK_FP32_VALU / 1e12,

@@ -14,6 +14,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import statistics
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -33,9 +34,9 @@ def kernel_sha(sources=KERNEL_SOURCES):
 
 
 def _short(name):
-    for key in ("wkv7_bwd_kernel", "wkv7_fwd_kernel", "fill_kernel", "copy"):
-        if key in name:
-            return key if key != "copy" else name[:60]
+    m = re.search(r"(wkv7_\w+_kernel|fill_kernel)", name)
+    if m:
+        return m.group(1)
     return name[:60]
 
 
