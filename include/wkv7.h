@@ -61,11 +61,13 @@ typedef enum {
 } wkv7_dtype;
 
 /* How wkv7_backward computes the gradients (the results agree to rounding).
- *   AUTO    : the chunk form where it applies (N = 64 and C = 64), the step
- *             scan elsewhere.
+ *   AUTO    : the chunk form where it applies (N = 64, C = 64 and
+ *             T*H*64*4 < 2^31 bytes), the step scan elsewhere.
  *   SCAN    : the step-by-step reverse scan: regenerate the states of a
  *             chunk from its checkpoint, then run the reverse recurrence.
- *   CHUNKED : the chunk form (WKV7_ERR_UNSUPPORTED where it does not apply).
+ *   CHUNKED : the chunk form (WKV7_ERR_UNSUPPORTED where it does not apply,
+ *             and where T*H*64*4 bytes, one batch row of a vector tensor,
+ *             reach 2^31).
  *             Per 64-step chunk it runs only dsa = G b step by step and forms
  *             every gradient from dense products of the chunk's vectors with
  *             the checkpointed state and the incoming state gradient.  It

@@ -184,7 +184,9 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
                           (const void *)ds0})
         if (!aligned(p)) return WKV7_ERR_INVALID;
 
-    if (d.algo == WKV7_ALGO_CHUNKED && !(d.N == 64 && d.C == 64)) return WKV7_ERR_UNSUPPORTED;
+    if (d.algo == WKV7_ALGO_CHUNKED &&
+        !(d.N == 64 && d.C == 64 && (d.T == 0 || wkv7::chunk_offsets_fit(d.T, d.H))))
+        return WKV7_ERR_UNSUPPORTED;
     if (d.T == 0) {
         if (!ds0) return WKV7_OK;
         return hip_status(wkv7::launch_fill(ds0, dsT, d.state_elems, stream));

@@ -230,6 +230,11 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
     const int64_t stride = H * 64;
     const int64_t vbase = (bidx * T * H + head) * 64;
     const int nck = p.nck;
+    // bytes of this (b, h)'s steps in a [B][T][H][64] tensor, from step 0:
+    // buffer accesses past them (the tail of a partial last chunk) read
+    // zeros and drop stores
+    const uint32_t vext = (uint32_t)(((T - 1) * stride + 64) * 4);
+    const uint32_t ustride = (uint32_t)stride;
     // every phase-2 tile of this lane is in feature column jw; state
     // gradients are held as rows 16 g + 4 ib + i of column jw, ib = 2 half + lb
     int l16 = lane & 15, g = lane >> 4, jw = fb * 16 + (lane & 15), ltid = tid;
@@ -279,7 +284,8 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
-            if (t < Lcc) pre[q][m] = InQuad<TIn>::load(src_[q] + vbase + (tt0 + t) * stride + j4);
+            pre[q][m] = InQuad<TIn>::bload(raw_buffer(src_[q] + vbase, vext * sizeof(TIn) / 4),
+                                           (uint32_t)(((uint32_t)tt0 + t) * ustride + j4) * sizeof(TIn));
         }
     };
     auto commit_regs = [&](int Lcc, int q) {
@@ -613,8 +619,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
-                saR[m] = t < Lc ? *reinterpret_cast<const float4 *>(p.sa + vbase + (t0 + t) * stride + j4)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
+                saR[m] = bload4(raw_buffer(p.sa + vbase, vext), (((uint32_t)t0 + t) * ustride + j4) * 4);
             }
 
             // One pass over the Grams of the value-side vectors in sVS (v,
@@ -682,9 +687,11 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             // ---- pass 2: Grams dy sa^T, dsa sa^T (dk written beside them);
             // db bracket; bt terms of dr, da; then the per-block sums of
             // k dk + b db - r dr - a da for the dw prefix
-            const int64_t cb = vbase + t0 * stride;   // this chunk's outputs
-            float *odk = p.dk + cb, *odb = p.db + cb, *odr = p.dr + cb;
-            float *oda = p.da + cb, *odw = p.dw + cb, *odv = p.dv + cb;
+            // this (b, h)'s outputs; element (t0 + t, jw) at byte offset ooff(t)
+            const BufRsrc odk = raw_buffer(p.dk + vbase, vext), odb = raw_buffer(p.db + vbase, vext);
+            const BufRsrc odr = raw_buffer(p.dr + vbase, vext), oda = raw_buffer(p.da + vbase, vext);
+            const BufRsrc odw = raw_buffer(p.dw + vbase, vext), odv = raw_buffer(p.dv + vbase, vext);
+            auto ooff = [&](int t) { return (((uint32_t)t0 + t) * ustride + jw) * 4; };
             gram(sDY, sD, sVS, [&](int k) {
                 if (k > 1) return;
                 const int tb = TB[k];
@@ -692,7 +699,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                 for (int i = 0; i < 4; ++i) {
                     const int t = 16 * tb + 4 * g + i;
                     const float gt = sG[A.col[i] + 1024 * tb];
-                    if (t < Lc) odk[t * (int)stride + jw] = XK[k][i] * __builtin_amdgcn_rcpf(gt);
+                    bstore(odk, ooff(t), XK[k][i] * __builtin_amdgcn_rcpf(gt));
                 }
             });
             __syncthreads();
@@ -748,13 +755,11 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                     const float inv = __builtin_amdgcn_rcpf(gt);
                     const float adA = sA[o] * XA[lt][i];
                     const float wdw = (cj + ex) - adA;
-                    if (t < Lc) {
-                        const int off = t * (int)stride + jw;
-                        odb[off] = XB[lt][i] * inv;
-                        odr[off] = XR[lt][i] * gt;
-                        oda[off] = XA[lt][i] * gp;
-                        odw[off] = wdw * gp * inv;
-                    }
+                    const uint32_t off = ooff(t);
+                    bstore(odb, off, XB[lt][i] * inv);
+                    bstore(odr, off, XR[lt][i] * gt);
+                    bstore(oda, off, XA[lt][i] * gp);
+                    bstore(odw, off, wdw * gp * inv);
                     ex += f[lt][i];
                 }
             };
@@ -800,7 +805,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = 16 * TB[lt] + 4 * g + i;
-                    if (t < Lc) odv[t * (int)stride + jw] = XV[lt][i];
+                    bstore(odv, ooff(t), XV[lt][i]);
                 }
             __syncthreads();
             refresh();
@@ -846,7 +851,7 @@ hipError_t launch_bwdc_t(const BwdLaunch &a, int *flags, hipStream_t stream)
 
 bool chunked_backward_supported(const BwdLaunch &a)
 {
-    return a.N == 64 && a.chunk == 64 && a.T > 0;
+    return a.N == 64 && a.chunk == 64 && chunk_offsets_fit(a.T, a.H);
 }
 
 hipError_t launch_backward_chunked(const BwdLaunch &a, int *flags, hipStream_t stream)

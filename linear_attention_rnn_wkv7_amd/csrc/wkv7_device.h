@@ -65,12 +65,55 @@ __device__ __forceinline__ float swap_add16(float x, float y)
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
 
+// Raw (untyped) buffer view of `bytes` bytes at `base`.  A buffer load at a
+// per-lane byte offset >= bytes returns zeros and a store there is dropped,
+// so the tail of a partial chunk needs no per-lane branch.  The range check
+// applies to the per-lane offset only: every varying part of an address goes
+// there, the scalar offset stays 0.  Word 3 is the gfx9 descriptor word for
+// 32-bit untyped data.
+constexpr int kRawBufferWord3 = 0x00020000;
+using BufRsrc = __amdgpu_buffer_rsrc_t;
+
+__device__ __forceinline__ BufRsrc raw_buffer(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRawBufferWord3);
+}
+
+// (the builtin's data operand is an unsigned int: pass the bits, not the
+// value converted)
+__device__ __forceinline__ void bstore(BufRsrc r, uint32_t off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)off, 0, 0);
+}
+
+// 16-byte buffer load through the fp32 form of the intrinsic: this compiler
+// lowers the integer 128-bit and 96-bit forms (__builtin_amdgcn_raw_buffer_
+// load_b128 / _b96) to a single-dword load (seen in the generated code).
+typedef float BufF4 __attribute__((ext_vector_type(4)));
+__device__ BufF4 raw_buffer_load_f32x4(BufRsrc rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.load.v4f32");
+
+__device__ __forceinline__ float4 bload4(BufRsrc r, uint32_t off)
+{
+    const BufF4 q = raw_buffer_load_f32x4(r, (int)off, 0, 0);
+    return make_float4(q.x, q.y, q.z, q.w);
+}
+
+__device__ __forceinline__ uint2 bload2(BufRsrc r, uint32_t off)
+{
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    const u2 q = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return make_uint2(q.x, q.y);
+}
+
 // 4 consecutive input elements, loaded raw (fp32: 16 bytes, bf16: 8 bytes)
 // and widened to fp32.
 template <typename TIn>
 struct InQuad {
     using raw = float4;
     __device__ static raw load(const TIn *p) { return *reinterpret_cast<const float4 *>(p); }
+    __device__ static raw bload(BufRsrc r, uint32_t off) { return bload4(r, off); }
     __device__ static float4 f32(raw q) { return q; }
 };
 
@@ -78,6 +121,7 @@ template <>
 struct InQuad<uint16_t> {   // bf16 stored as raw 16-bit patterns
     using raw = uint2;
     __device__ static raw load(const uint16_t *p) { return *reinterpret_cast<const uint2 *>(p); }
+    __device__ static raw bload(BufRsrc r, uint32_t off) { return bload2(r, off); }
     __device__ static float4 f32(raw q)
     {
         return make_float4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y));

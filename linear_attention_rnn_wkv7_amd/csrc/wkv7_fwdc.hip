@@ -362,22 +362,27 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
         constexpr bool kDma = std::is_same<TIn, float>::value;
         using Raw = typename InQuad<TIn>::raw;
         Raw pre[12];
+        auto stage_unit = [&](int64_t t0, int b, int k) {
+            const int unit = 12 * h + k, v = unit >> 3, u = unit & 7;
+            const TIn *base = in_ptr[v] + (t0 + 4 * u) * stride;
+            if constexpr (kDma) {
+                const unsigned lds = (unsigned)(uintptr_t)(
+                    const __attribute__((address_space(3))) float *)&slot[b][v][u * 256];
+                dma16_split(base, 4u * (unsigned)Ld[u & 3], lds);
+            } else {
+                pre[k] = InQuad<TIn>::load(base + Ld[u & 3]);
+            }
+        };
         auto stage_issue = [&](int64_t blk, int b) {
             const int nst = steps_of(blk);
             const int64_t t0 = blk * kTB;
+            if (nst == kTB) {   // a full block: no per-lane condition
 #pragma unroll
-            for (int k = 0; k < 12; ++k) {
-                const int unit = 12 * h + k, v = unit >> 3, u = unit & 7;
-                const TIn *base = in_ptr[v] + (t0 + 4 * u) * stride;
-                if (nst == kTB || 4 * u + g < nst) {
-                    if constexpr (kDma) {
-                        const unsigned lds = (unsigned)(uintptr_t)(
-                            const __attribute__((address_space(3))) float *)&slot[b][v][u * 256];
-                        dma16_split(base, 4u * (unsigned)Ld[u & 3], lds);
-                    } else {
-                        pre[k] = InQuad<TIn>::load(base + Ld[u & 3]);
-                    }
-                }
+                for (int k = 0; k < 12; ++k) stage_unit(t0, b, k);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 12; ++k)
+                    if (4 * ((12 * h + k) & 7) + g < nst) stage_unit(t0, b, k);
             }
         };
         auto stage_land = [&](int64_t blk, int b) {
@@ -577,10 +582,16 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
             if (!sa_out) return;
             const int nst = steps_of(blk);
             float *dst = sa_out + (blk * kTB + 4 * h) * stride;
+            if (nst == kTB) {
 #pragma unroll
-            for (int k = 0; k < 2; ++k)
-                if (nst == kTB || 4 * h + 16 * k + g < nst)
+                for (int k = 0; k < 2; ++k)
                     *reinterpret_cast<float4 *>(dst + 16 * k * stride + Ls) = lds4(sap[b] + 256 * h + 1024 * k, Lq);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+                    if (4 * h + 16 * k + g < nst)
+                        *reinterpret_cast<float4 *>(dst + 16 * k * stride + Ls) = lds4(sap[b] + 256 * h + 1024 * k, Lq);
+            }
         };
         auto ckpt_out = [&](int64_t blk) {
             const int64_t t = blk * kTB;

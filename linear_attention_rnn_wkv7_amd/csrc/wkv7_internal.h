@@ -36,6 +36,13 @@ struct BwdLaunch {
     int algo;                // wkv7_algo
 };
 
+// The chunk forms address one (b) slice of a [B][T][H][64] tensor with
+// 32-bit byte offsets: T * H * 64 * 4 must stay below 2^31.
+inline bool chunk_offsets_fit(int64_t T, int64_t H)
+{
+    return T > 0 && H > 0 && T <= (int64_t(1) << 31) / (H * 64 * 4) - 1;
+}
+
 // Bytes of sub-checkpoint scratch the backward needs for a shape.
 size_t sub_bytes(int64_t B, int64_t H, int64_t N, int chunk);
 
