@@ -18,17 +18,17 @@
 // products, done with v_mfma_f32_16x16x4f32.
 //
 // One workgroup of eight waves per (b, h).  Waves 0-3 run the steps of block
-// q (wave w: rows 16 w .. 16 w + 15 of S, 2 rows x 8 columns per lane).
-// Waves 4-7 ("helpers") meanwhile copy block q + 1 into LDS, rescale it and
-// compute its Gram tiles, c and sum of v kt^T; they also finish y of block
-// q - 1 (which needs its sa) and start y of block q (which needs S0), and
-// write the sa tape and the checkpoints.  The helpers synchronise among
-// themselves through an LDS arrival counter, and with the scan waves twice
-// per block (X: the block's steps are done; Y: the state after the block is
-// in LDS).  Blocks whose decays leave [1/16, 1] or whose cumulative decay
-// drops below 2^-60, and a final partial block, run the plain step on the
-// scan waves instead (y on the VALU, no rescaling).  Checkpoints must fall
-// on block starts (chunk a multiple of 32).
+// q (wave w: rows 16 w .. 16 w + 15 of S, 2 rows x 8 columns per lane) and
+// then its y for their rows on the matrix cores.  Waves 4-7 ("helpers")
+// meanwhile copy block q + 1 into LDS, rescale it and compute its Gram
+// tiles, c and sum of v kt^T; they also write the sa tape of block q - 1 and
+// the checkpoints.  The helpers synchronise among themselves through an LDS
+// arrival counter, and with the scan waves twice per block (X: the block's
+// steps are done; Y: the state after the block is in LDS, and the scan waves
+// hold the next block's Gram tiles for y).  Blocks whose decays leave
+// [1/16, 1] or whose cumulative decay drops below 2^-60, and a final partial
+// block, run the plain step on the scan waves instead (y on the VALU, no
+// rescaling).  Checkpoints must fall on block starts (chunk a multiple of 32).
 
 #include <type_traits>
 
@@ -172,8 +172,81 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
             if (cg < R) *base_row_t = val;
         };
 
+        // The read-out y of a rescaled block, on the matrix cores: tile tb
+        // holds steps 16 tb .. 16 tb + 15 (accumulator row 4 gq + i) of rows
+        // 16 wave .. 16 wave + 15 of S (accumulator column l16).
+        const bool want_y = p.y != nullptr;
+        const int l16 = lane & 15, gq = lane >> 4, qa = l16 >> 2, c3 = l16 & 3;
+        // rows 16 X + l16, columns 16 q4 + 4 gq .. + 3:  L1[q4] + 1024 X
+        int L1[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) L1[q4] = 64 * l16 + 16 * (q4 ^ qa) + 4 * (gq ^ c3);
+        // rows 16 U + 4 gq + r, column 16 wave + l16:  Lv[r] + 1024 U
+        int Lv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Lv[r] = 256 * gq + 64 * r + 16 * (wave ^ gq) + 4 * (qa ^ r) + c3;
+        // Gram tiles kt.rb and bt.rb of the next block, (u-block, t-block)
+        // = (0,0), (0,1), (1,1); read while the helpers leave them in place
+        f4 Pk[3], Pb[3];
+        auto read_grams = [&]() {
+#pragma unroll
+            for (int pos = 0; pos < 3; ++pos) {
+                Pk[pos] = *reinterpret_cast<const f4 *>(&gram[3 + pos][4 * lane]);
+                Pb[pos] = *reinterpret_cast<const f4 *>(&gram[6 + pos][4 * lane]);
+            }
+        };
+        // y_t = S0 rb_t + sum_{u<=t} v_u (kt_u . rb_t) + sa_u (bt_u . rb_t)
+        auto y_block = [&](int bb, int64_t t0) {
+            const float *rbv = slot[bb][vR], *vv = slot[bb][vV], *sav = sap[bb];
+            float4 sr[4], xr[2][4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                sr[q4] = lds4(sS0 + 1024 * wave, L1[q4]);
+                xr[0][q4] = lds4(rbv, L1[q4]);
+                xr[1][q4] = lds4(rbv + 1024, L1[q4]);
+            }
+            float vb[2][4], sb[2][4];
+#pragma unroll
+            for (int ub = 0; ub < 2; ++ub)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    vb[ub][r] = vv[1024 * ub + Lv[r]];
+                    sb[ub][r] = sav[1024 * ub + Lv[r]];
+                }
+            f4 Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) Y[tb] = mfma(xr[tb][q4].x, sr[q4].x, Y[tb]);
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) Y[tb] = mfma(xr[tb][q4].y, sr[q4].y, Y[tb]);
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) Y[tb] = mfma(xr[tb][q4].z, sr[q4].z, Y[tb]);
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) Y[tb] = mfma(xr[tb][q4].w, sr[q4].w, Y[tb]);
+            }
+#pragma unroll
+            for (int ub = 0; ub < 2; ++ub)
+#pragma unroll
+                for (int tb = ub; tb < 2; ++tb) {
+                    const int pos = tb == 0 ? 0 : 1 + ub;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        Y[tb] = mfma(Pk[pos][r], vb[ub][r], Y[tb]);
+                        Y[tb] = mfma(Pb[pos][r], sb[ub][r], Y[tb]);
+                    }
+                }
+            float *dst = p.y + vbase + t0 * stride + 16 * wave + l16;
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[(16 * tb + 4 * gq + i) * stride] = Y[tb][i];
+        };
+
         put_state();
         __syncthreads();   // block 0 ready, S0 in LDS
+        read_grams();
+        __syncthreads();   // the helpers may now replace the Gram tiles
 
         for (int64_t q = 0; q < nblk; ++q) {
             const int bb = (int)(q & 1);
@@ -217,6 +290,7 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                         for (int c = 0; c < CC; ++c) S[e][c] = fmaf(sa[e], o.bt[c], S[e][c]);
                     park(&SA[sw(s, row0 + cg)], sa);
                 }
+                if (want_y) y_block(bb, t0);
                 __syncthreads();   // X: steps done; sum v kt^T is in LDS
                 float gr[CC];
                 {
@@ -271,6 +345,7 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                 __syncthreads();   // X
             }
             put_state();           // the state before block q + 1
+            read_grams();          // (block q + 1's, computed during block q)
             __syncthreads();       // Y
         }
         if (p.sT) {
@@ -291,11 +366,9 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
     // offsets plus a constant, so that the helpers spend their issue slots
     // on loads, stores and MFMAs rather than on address arithmetic.
     const int l16 = lane & 15, g = lane >> 4, qa = l16 >> 2, c3 = l16 & 3;
-    const bool want_y = p.y != nullptr;
     const TIn *in_ptr[6];
 #pragma unroll
     for (int v = 0; v < 6; ++v) in_ptr[v] = p.in[v] + vbase;
-    float *const y_out = p.y ? p.y + vbase : nullptr;
     float *const sa_out = p.sa ? p.sa + vbase : nullptr;
     float *const ck_out = p.ckpt;
     const int chunk = p.chunk, nck = p.nck;
@@ -349,7 +422,6 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
         // tape and checkpoints: rows 4 h + 16 k + g, columns 4 l16 .. + 3
         const int Lq = 64 * g + 4 * (l16 ^ (4 * h + g));
         // global offsets (elements)
-        const int Ly = 4 * g * (int)stride + l16;   // y: step 4 g, row l16
         const int Ls = g * (int)stride + 4 * l16;   // tape: step g, column 4 l16
         int Ld[4];                                  // staging: step g, swizzled column
 #pragma unroll
@@ -523,61 +595,11 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
             return *reinterpret_cast<const f4 *>(&gram[3 * kind + pos][4 * lane]);
         };
 
-        f4 Y[2], Yv[2], VK[4], PbA[2], PbB[2], PbC[2];
-        bool fastA = false, fastB = false;   // blocks q - 1 and q
-#pragma unroll
-        for (int m = 0; m < 2; ++m) Y[m] = Yv[m] = PbA[m] = PbB[m] = PbC[m] = f4{0.f, 0.f, 0.f, 0.f};
+        f4 VK[4];
+        bool fastB = false;   // block q
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) VK[jt] = f4{0.f, 0.f, 0.f, 0.f};
 
-        // y of a block from its S0: Y = Yv + S0 rb_t
-        auto y_from_s0 = [&](int b) {
-            const float *xs = &slot[b][vR][1024 * tb];
-            float4 xr[4], sr[2][4];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                xr[q4] = lds4(xs, L1[q4]);
-#pragma unroll
-                for (int m = 0; m < 2; ++m) sr[m][q4] = lds4(sS0 + 1024 * (2 * ih + m), L1[q4]);
-            }
-#pragma unroll
-            for (int m = 0; m < 2; ++m) Y[m] = Yv[m];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-#pragma unroll
-                for (int m = 0; m < 2; ++m) Y[m] = mfma(xr[q4].x, sr[m][q4].x, Y[m]);
-#pragma unroll
-                for (int m = 0; m < 2; ++m) Y[m] = mfma(xr[q4].y, sr[m][q4].y, Y[m]);
-#pragma unroll
-                for (int m = 0; m < 2; ++m) Y[m] = mfma(xr[q4].z, sr[m][q4].z, Y[m]);
-#pragma unroll
-                for (int m = 0; m < 2; ++m) Y[m] = mfma(xr[q4].w, sr[m][q4].w, Y[m]);
-            }
-        };
-        // the sa terms of the block whose sa is in sap[b]:
-        // Y += sum_u (bt_u . rb_t) sa_u
-        auto y_from_sa = [&](int b) {
-            float sv[2][2][4];
-#pragma unroll
-            for (int ub = 0; ub <= tb; ++ub)
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sv[ub][m][r] = sap[b][1024 * ub + L2[m][r]];
-#pragma unroll
-            for (int ub = 0; ub <= tb; ++ub)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int m = 0; m < 2; ++m) Y[m] = mfma(PbA[ub][r], sv[ub][m][r], Y[m]);
-        };
-        auto y_store = [&](int64_t t0) {
-            float *dst = y_out + (t0 + 16 * tb) * stride + 32 * ih;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int m = 0; m < 2; ++m) dst[Ly + r * stride + 16 * m] = Y[m][r];
-        };
         auto tape_out = [&](int64_t blk, int b) {
             if (!sa_out) return;
             const int nst = steps_of(blk);
@@ -618,17 +640,8 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                 stage_issue(q + 1, bn);
                 if (h == 0 && lane == 0) hbad[bn] = 0;
             }
-            if (q >= 1) {
-                if (fastA && want_y) {
-                    y_from_sa(bn);
-                    y_store((q - 1) * kTB);
-                }
-                tape_out(q - 1, bn);
-            }
-            if (q >= 0) {
-                ckpt_out(q);
-                if (fastB && want_y) y_from_s0(bb);
-            }
+            if (q >= 1) tape_out(q - 1, bn);
+            if (q >= 0) ckpt_out(q);
             bool fastC = false;
             if (next) {
                 stage_land(q + 1, bn);
@@ -640,14 +653,10 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                     hsync();   // block q + 1 rescaled
                     grams(sb);
                     hsync();   // Gram tiles in LDS
-                    f4 Mk[2], Pk[2];
+                    f4 Mk[2];
 #pragma unroll
-                    for (int ub = 0; ub <= tb; ++ub) {
-                        Mk[ub] = gram_get(0, ub);
-                        Pk[ub] = gram_get(1, ub);
-                        PbC[ub] = gram_get(2, ub);
-                    }
-                    // c (into the slot of w) and the v terms of y
+                    for (int ub = 0; ub <= tb; ++ub) Mk[ub] = gram_get(0, ub);
+                    // c, into the slot of w
                     float vb[2][2][4];
 #pragma unroll
                     for (int ub = 0; ub <= tb; ++ub)
@@ -663,18 +672,15 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
 #pragma unroll
                         for (int jt = 0; jt < 4; ++jt) kb[kk][jt] = sb[vK * 2048 + L3 + 256 * kk + 16 * (jt ^ (kk & 3))];
                     }
-                    f4 cacc[2], yacc[2];
+                    f4 cacc[2];
 #pragma unroll
-                    for (int m = 0; m < 2; ++m) cacc[m] = yacc[m] = f4{0.f, 0.f, 0.f, 0.f};
+                    for (int m = 0; m < 2; ++m) cacc[m] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ub = 0; ub <= tb; ++ub)
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
 #pragma unroll
-                            for (int m = 0; m < 2; ++m) {
-                                cacc[m] = mfma(Mk[ub][r], vb[ub][m][r], cacc[m]);
-                                yacc[m] = mfma(Pk[ub][r], vb[ub][m][r], yacc[m]);
-                            }
+                            for (int m = 0; m < 2; ++m) cacc[m] = mfma(Mk[ub][r], vb[ub][m][r], cacc[m]);
 #pragma unroll
                     for (int jt = 0; jt < 4; ++jt) VK[jt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -683,7 +689,6 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                         for (int jt = 0; jt < 4; ++jt) VK[jt] = mfma(va[kk], kb[kk][jt], VK[jt]);
 #pragma unroll
                     for (int m = 0; m < 2; ++m) {
-                        Yv[m] = yacc[m];
                         float *cs = &slot[bn][vW][1024 * tb];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) cs[L2[m][r]] = cacc[m][r];
@@ -695,24 +700,12 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                 __syncthreads();   // Y: the state after block q in LDS
             } else {
                 __syncthreads();   // block 0 ready, S0 in LDS
+                __syncthreads();   // the scan waves hold block 0's Gram tiles
             }
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                PbA[m] = PbB[m];
-                PbB[m] = PbC[m];
-            }
-            fastA = fastB;
             fastB = fastC;
         }
-        // the last block's sa terms of y and its tape
-        if (nblk > 0) {
-            const int bl = (int)((nblk - 1) & 1);
-            if (fastA && want_y) {
-                y_from_sa(bl);
-                y_store((nblk - 1) * kTB);
-            }
-            tape_out(nblk - 1, bl);
-        }
+        // the last block's tape
+        if (nblk > 0) tape_out(nblk - 1, (int)((nblk - 1) & 1));
     };
     switch (wave) {
     case 4: helper(std::integral_constant<int, 0>{}); break;
