@@ -212,7 +212,6 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
     // two Gram matrices (10 lower 16x16 tiles each)
     __shared__ __align__(16) float sP[20 * 256];
     __shared__ __align__(16) float sScan[4][256];
-    __shared__ __align__(16) float sCp[8][64];
     __shared__ __align__(16) float sCj[2][64];
     // inverses of the four diagonal 16x16 blocks of the dsa system
     __shared__ __align__(16) float sTT[4 * 256];
@@ -333,20 +332,26 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         __syncthreads();
         refresh();
 
-        // ---- cumulative decay, in place of w: 8 segments of 8 steps per column
+        // ---- cumulative decay, in place of w.  Wave w takes columns
+        // 8 w .. 8 w + 7; lane (seg, c) the steps 8 seg .. 8 seg + 7 of column
+        // 8 w + c: the product over its segment, then the product over the
+        // earlier segments by a scan across the lanes (no barrier needed)
         {
-            const int j = ltid & 63, seg = ltid >> 6;
+            const int c = ltid & 7, seg = (ltid >> 3) & 7, j = (ltid >> 6) * 8 + c;
+            const int ln = ltid & 63;
             float pr = 1.f;
 #pragma unroll
             for (int u = 0; u < 8; ++u) pr *= sG[sw(seg * 8 + u, j)];
-            sCp[seg][j] = pr;
-        }
-        __syncthreads();
-        refresh();
-        {
-            const int j = ltid & 63, seg = ltid >> 6;
-            float pre_ = 1.f;
-            for (int s2 = 0; s2 < seg; ++s2) pre_ *= sCp[s2][j];
+            float inc = pr;   // product over segments 0 .. seg
+#pragma unroll
+            for (int d = 1; d < 8; d *= 2) {
+                const float o = __builtin_bit_cast(
+                    float, __builtin_amdgcn_ds_bpermute(4 * ((ln - 8 * d) & 63), __builtin_bit_cast(int, inc)));
+                inc = seg >= d ? inc * o : inc;
+            }
+            const float before = __builtin_bit_cast(
+                float, __builtin_amdgcn_ds_bpermute(4 * ((ln - 8) & 63), __builtin_bit_cast(int, inc)));
+            float pre_ = seg >= 1 ? before : 1.f;
             bool ok = true;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
