@@ -61,11 +61,15 @@ __device__ __forceinline__ int sw(int t, int j)
     return (t << 6) + ((((j >> 2) ^ (t & 15))) << 2) + (j & 3);
 }
 
-// 16x16 tile of a Gram matrix: rows a, b: quarter-rotated so that the four
-// rows an MFMA result writes at once fall in different banks.
+// Element (a, b) of a 16x16 tile of a Gram matrix.  Rows a = 4 g + s (g the
+// lane's row group, s fixed) and columns b = 4 g + s both fall in 64
+// distinct banks of the 64-bank LDS: the row's low bits select a 64-float
+// quarter, its high bits a 16-float row within it, and they scramble the
+// column (b ^ 5 (a & 3)).  Within a row, each aligned group of four
+// columns stays together (permuted by a & 3).
 __device__ __forceinline__ int pt(int a, int b)
 {
-    return ((a >> 2) << 6) + ((((a & 3) + (a >> 2)) & 3) << 4) + b;
+    return ((a & 3) << 6) + ((a >> 2) << 4) + (b ^ (5 * (a & 3)));
 }
 
 // Lower-triangular 16x16 block (ab >= bb) of a 64x64 matrix -> slot 0..9.
@@ -110,11 +114,11 @@ __device__ __forceinline__ void row16(const float *s, int t, int c0, float (&o)[
 //   col[s]  : element (16 ub + 4 g + s, jw) of a [64][64] array, minus 1024 ub
 //   rowb[m] : float4 (16 tb + l16, 16 g + 4 m .. +3), minus 1024 tb
 //   pa[s]   : Gram tile element (4 g + s, l16)
-//   pb      : Gram tile element (l16, 4 g) (then + s)
+//   pb[s]   : Gram tile element (l16, 4 g + s)
 //   hrow    : element (16 ub + 4 g + s, 16 (l16 / 4) + 4 ib + l16 % 4) minus
 //             1024 ub + 64 s + 4 (ib ^ s)
 struct LaneAddr {
-    int col[4], rowb[4], pa[4], pb, hrow;
+    int col[4], rowb[4], pa[4], pb[4], hrow;
 };
 
 __device__ __forceinline__ LaneAddr lane_addr(int l16, int g, int jw)
@@ -124,9 +128,9 @@ __device__ __forceinline__ LaneAddr lane_addr(int l16, int g, int jw)
     for (int s = 0; s < 4; ++s) {
         a.col[s] = 64 * (4 * g + s) + ((((jw >> 2) ^ (4 * g + s)) & 15) << 2) + (jw & 3);
         a.rowb[s] = 64 * l16 + ((((4 * g + s) ^ l16) & 15) << 2);
-        a.pa[s] = 64 * g + (((s + g) & 3) << 4) + l16;
+        a.pa[s] = pt(4 * g + s, l16);
+        a.pb[s] = pt(l16, 4 * g + s);
     }
-    a.pb = ((l16 >> 2) << 6) + ((((l16 & 3) + (l16 >> 2)) & 3) << 4) + 4 * g;
     a.hrow = 256 * g + (((l16 >> 2) ^ g) << 4) + (l16 & 3);
     return a;
 }
@@ -447,7 +451,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         // Gram tile slot elements (4 g + s, l16) and (l16, 4 g + s), and
         // element (16 ub + 4 g + s, jw) of an array
         auto tA = [&](int slot, int s) { return sP[slot * 256 + A.pa[s]]; };
-        auto tAt = [&](int slot, int s) { return sP[slot * 256 + A.pb + s]; };
+        auto tAt = [&](int slot, int s) { return sP[slot * 256 + A.pb[s]]; };
         auto colE = [&](const float *arr, int ub, int s) { return arr[A.col[s] + 1024 * ub]; };
 
         auto body = [&](auto hc) {
@@ -537,7 +541,14 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                 for (int i = 0; i < 4; ++i) X[i] = (4 * g + i == l16) ? 1.f : 0.f;
                 // the coefficient rows are read four steps ahead of the chain
                 float4 m[4];
-                auto mrow = [&](int tl) { return lds4(sP, slot * 256 + pt(tl, 0) + 4 * g); };
+                // row tl, columns 4 g .. 4 g + 3 (stored as one aligned group,
+                // column 4 g + j in component j ^ (tl & 3))
+                auto mrow = [&](int tl) {
+                    const float4 q = lds4(sP, slot * 256 + (pt(tl, 4 * g) & ~3));
+                    const float c[4] = {q.x, q.y, q.z, q.w};
+                    const int x = tl & 3;
+                    return make_float4(c[x], c[1 ^ x], c[2 ^ x], c[3 ^ x]);
+                };
 #pragma unroll
                 for (int tl = 15; tl >= 12; --tl) m[tl & 3] = mrow(tl);
 #pragma unroll
@@ -566,7 +577,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                     constexpr int tb = decltype(tbc)::value;
                     f4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) x = mfma(sTT[tb * 256 + A.pb + s], Rt[tb][s], x);
+                    for (int s = 0; s < 4; ++s) x = mfma(sTT[tb * 256 + A.pb[s]], Rt[tb][s], x);
                     Rt[tb] = x;
 #pragma unroll
                     for (int tp = 0; tp < tb; ++tp)
