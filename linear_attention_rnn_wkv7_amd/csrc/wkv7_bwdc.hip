@@ -54,11 +54,20 @@ __device__ __forceinline__ f4 mfma(float a, float b, f4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// [64][64] fp32 LDS arrays, 16-byte groups of a row XOR-swizzled by the row:
-// rows and 16-row column slices both read without bank conflicts.
+// [64][64] fp32 LDS arrays, the 16-byte groups of row t XOR-swizzled by
+// xs(t & 15).  With x = 4 x_hi + x_lo, xs(x) = 4 (x_lo ^ x_hi) + x_hi: both
+// access shapes of the kernel meet 64 distinct banks of the 64-bank LDS (as
+// measured with the LDS bank-conflict counter): 16-byte reads of 16 rows
+// t..t+15, each lane its own row (16 lanes per row group), and 4-byte reads
+// of the 16 columns of a 16-column block in rows t + 4 g + s.
+__device__ __forceinline__ int xs(int x)
+{
+    return (((x & 3) ^ (x >> 2)) << 2) + (x >> 2);
+}
+
 __device__ __forceinline__ int sw(int t, int j)
 {
-    return (t << 6) + ((((j >> 2) ^ (t & 15))) << 2) + (j & 3);
+    return (t << 6) + ((((j >> 2) ^ xs(t & 15))) << 2) + (j & 3);
 }
 
 // Element (a, b) of a 16x16 tile of a Gram matrix.  Rows a = 4 g + s (g the
@@ -115,10 +124,8 @@ __device__ __forceinline__ void row16(const float *s, int t, int c0, float (&o)[
 //   rowb[m] : float4 (16 tb + l16, 16 g + 4 m .. +3), minus 1024 tb
 //   pa[s]   : Gram tile element (4 g + s, l16)
 //   pb[s]   : Gram tile element (l16, 4 g + s)
-//   hrow    : element (16 ub + 4 g + s, 16 (l16 / 4) + 4 ib + l16 % 4) minus
-//             1024 ub + 64 s + 4 (ib ^ s)
 struct LaneAddr {
-    int col[4], rowb[4], pa[4], pb[4], hrow;
+    int col[4], rowb[4], pa[4], pb[4];
 };
 
 __device__ __forceinline__ LaneAddr lane_addr(int l16, int g, int jw)
@@ -126,12 +133,11 @@ __device__ __forceinline__ LaneAddr lane_addr(int l16, int g, int jw)
     LaneAddr a;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        a.col[s] = 64 * (4 * g + s) + ((((jw >> 2) ^ (4 * g + s)) & 15) << 2) + (jw & 3);
-        a.rowb[s] = 64 * l16 + ((((4 * g + s) ^ l16) & 15) << 2);
+        a.col[s] = sw(4 * g + s, jw);
+        a.rowb[s] = sw(l16, 16 * g + 4 * s);
         a.pa[s] = pt(4 * g + s, l16);
         a.pb[s] = pt(l16, 4 * g + s);
     }
-    a.hrow = 256 * g + (((l16 >> 2) ^ g) << 4) + (l16 & 3);
     return a;
 }
 
@@ -308,7 +314,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         for (int k2 = 0; k2 < 2; ++k2) {
             const int blk = wave + 8 * k2;
             const int t = 4 * blk + ((ltid & 63) >> 4);
-            const int j4 = ((ltid & 15) ^ (t & 15)) << 2;
+            const int j4 = ((ltid & 15) ^ xs(t & 15)) << 2;
             dma16(reinterpret_cast<const float *>(src_[q]) + vbase + (tt0 + t) * stride + j4,
                   dst_[q] + blk * 256);
         }
@@ -489,7 +495,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                         b[0] = colE(sF, ub, s);
 #pragma unroll
                         for (int lb = 0; lb < 2; ++lb)
-                            b[1 + lb] = sX[A.hrow + 1024 * ub + 64 * s + 4 * ((2 * HF + lb) ^ s)];
+                            b[1 + lb] = sX[1024 * ub + sw(4 * g + s, 16 * (l16 >> 2) + 4 * (2 * HF + lb) + (l16 & 3))];
                     },
                     [&](int k, const float (&b)[6]) {
 #pragma unroll
