@@ -159,19 +159,19 @@ __device__ __forceinline__ void rowl(const float *s, const LaneAddr &A, int tb, 
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Runs mma(k, buf) for k = 0 .. N-1 with the operands of group k loaded by
-// load(k, buf) one group ahead into the other of two register buffers, so
-// that each group's LDS reads are in flight while the previous group's
-// MFMAs run.
-template <int N, int W, typename L, typename M>
+// load(k, buf) D groups ahead into one of D + 1 register buffers, so that
+// each group's LDS reads are in flight while the previous groups' MFMAs run.
+template <int N, int W, int D = 1, typename L, typename M>
 __device__ __forceinline__ void pipelined(L load, M mma)
 {
-    float buf[2][W];
-    load(0, buf[0]);
+    float buf[D + 1][W];
+#pragma unroll
+    for (int k = 0; k < D && k < N; ++k) load(k, buf[k]);
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         sched_fence();
-        if (k + 1 < N) load(k + 1, buf[(k + 1) & 1]);
-        mma(k, buf[k & 1]);
+        if (k + D < N) load(k + D, buf[(k + D) % (D + 1)]);
+        mma(k, buf[k % (D + 1)]);
     }
     sched_fence();
 }
