@@ -4,7 +4,9 @@
     python -m linear_attention_rnn_wkv7_amd.profiling traffic --fetch F.csv --write W.csv \
         --kernel wkv7_bwd_kernel --copy-bytes N --workload NAME --cmd "..." --out F.json
 
-`stats` condenses a --kernel-trace --stats kernel_stats.csv.  `traffic`
+`stats` condenses a --kernel-trace --stats kernel_stats.csv.  `sq` sums SQ
+and GRBM counters per dispatch of each wkv7 kernel (MFMA busy fraction, LDS
+bank-conflict cycles per CU).  `traffic`
 turns per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of a kernel into bytes per
 launch, scaling each counter by what it reads for the plain device copy of
 `copy-bytes` bytes that bench.py --copy-bytes runs in the same process.
@@ -54,6 +56,35 @@ def stats(csv_path, cmd, out):
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
     lines.append("")
     lines.append(f"Kernel sources sha: `{kernel_sha()}`")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out
+
+
+def sq(csv_path, cmd, out, n_simd=1024, n_cu=256, n_xcd=8):
+    sums, disp = {}, {}
+    for r in csv.DictReader(open(csv_path)):
+        m = re.search(r"(wkv7_\w+_kernel)", r["Kernel_Name"])
+        if not m:
+            continue
+        k = m.group(1)
+        key = (k, r["Counter_Name"])
+        sums[key] = sums.get(key, 0.0) + float(r["Counter_Value"])
+        disp.setdefault(k, set()).add(r["Dispatch_Id"])
+    lines = ["# rocprofv3 SQ counters per dispatch", "", "Command:", "", "```", cmd, "```", "",
+             "| kernel | counter | per dispatch |", "|---|---|---|"]
+    for (k, c), v in sorted(sums.items()):
+        lines.append(f"| `{k}` | {c} | {v / len(disp[k]):.4e} |")
+    lines += ["", "| kernel | MFMA busy / (active cycles x SIMDs) | LDS bank-conflict cycles per CU / active cycles |",
+              "|---|---|---|"]
+    for k in sorted(disp):
+        n = len(disp[k])
+        act = sums.get((k, "GRBM_GUI_ACTIVE"), 0.0) / n / n_xcd
+        mf = sums.get((k, "SQ_VALU_MFMA_BUSY_CYCLES"), 0.0) / n
+        bc = sums.get((k, "SQ_LDS_BANK_CONFLICT"), 0.0) / n
+        if act > 0:
+            lines.append(f"| `{k}` | {mf / (act * n_simd):.3f} | {bc / n_cu / act:.3f} |")
+    lines += ["", f"Kernel sources sha: `{kernel_sha()}`"]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     return out
@@ -112,6 +143,10 @@ if __name__ == "__main__":
     a.add_argument("--csv", required=True)
     a.add_argument("--cmd", required=True)
     a.add_argument("--out", required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("--csv", required=True)
+    q.add_argument("--cmd", required=True)
+    q.add_argument("--out", required=True)
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
@@ -123,6 +158,8 @@ if __name__ == "__main__":
     args = ap.parse_args()
     if args.what == "stats":
         print(stats(args.csv, args.cmd, args.out))
+    elif args.what == "sq":
+        print(sq(args.csv, args.cmd, args.out))
     else:
         print(json.dumps(traffic(args.fetch, args.write, args.kernel, args.copy_bytes,
                                  args.workload, args.cmd, args.out)))
