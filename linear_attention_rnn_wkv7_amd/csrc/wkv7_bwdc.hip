@@ -418,14 +418,11 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         // side(k) is independent work placed beside tile k's MFMAs.
         auto gram_store = [&](int n, f4 acc) {
             const int pr = n < 10 ? n : n - 10;
-            const bool diag = tab(pr) == tbb(pr);
+            // on a diagonal tile, rows al < l16 (first Gram) or al <= l16
+            // (second) are zero: rows al < lim, selected without branches
+            const int lim = tab(pr) != tbb(pr) ? 0 : n < 10 ? l16 : l16 + 1;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int al = 4 * g + i;
-                float val = acc[i];
-                if (diag && (n < 10 ? al < l16 : al <= l16)) val = 0.f;
-                sP[n * 256 + A.pa[i]] = val;
-            }
+            for (int i = 0; i < 4; ++i) sP[n * 256 + A.pa[i]] = 4 * g + i < lim ? 0.f : acc[i];
         };
         auto gram = [&](const float *sX1, const float *sX2, const float *sY, auto side) {
             float xa[16], ya[16], xb[16], yb[16];
