@@ -537,6 +537,10 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 #pragma unroll
                         for (int tb = 0; tb <= ub; ++tb) Rt[tb] = mfma(b[1 + tb], b[0], Rt[tb]);
                     });
+                // the second-half waves' block inverses take longer than
+                // the right-hand side: two dsa-free products fit beside them
+                pd_xk();
+                pd_xv();
             } else {
                 const int slot = 10 + tix(fb, fb);
                 f4 X;
@@ -589,13 +593,11 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                 };
                 // the dsa-free products fill the gaps of the dependent chain
                 apply_block(std::integral_constant<int, 3>{});
-                pd_xk();
-                apply_block(std::integral_constant<int, 2>{});
                 pd_xr();
+                apply_block(std::integral_constant<int, 2>{});
                 apply_block(std::integral_constant<int, 1>{});
-                pd_xv();
-                apply_block(std::integral_constant<int, 0>{});
                 pd_h();
+                apply_block(std::integral_constant<int, 0>{});
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
