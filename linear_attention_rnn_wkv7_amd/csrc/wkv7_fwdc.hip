@@ -17,18 +17,19 @@
 // with S0 the state before the block.  c, sum_u v_u kt_u^T and y are dense
 // products, done with v_mfma_f32_16x16x4f32.
 //
-// One workgroup of eight waves per (b, h).  Waves 0-3 run the steps of block
-// q (wave w: rows 16 w .. 16 w + 15 of S, 2 rows x 8 columns per lane) and
-// then its y for their rows on the matrix cores.  Waves 4-7 ("helpers")
-// meanwhile copy block q + 1 into LDS, rescale it and compute its Gram
-// tiles, c and sum of v kt^T; they also write the sa tape of block q - 1 and
+// One workgroup of twelve waves per (b, h).  Waves 0-3 run the steps of
+// block q (wave w: rows 16 w .. 16 w + 15 of S, 2 rows x 8 columns per
+// lane).  Waves 4-11 ("helpers", eight of them, two per SIMD beside one scan
+// wave) meanwhile copy block q + 1 into LDS, rescale it and compute its Gram
+// tiles, c and sum of v kt^T; they also finish y of block q - 1 (which needs
+// its sa) and start y of block q (which needs S0), and write the sa tape and
 // the checkpoints.  The helpers synchronise among themselves through an LDS
 // arrival counter, and with the scan waves twice per block (X: the block's
-// steps are done; Y: the state after the block is in LDS, and the scan waves
-// hold the next block's Gram tiles for y).  Blocks whose decays leave
-// [1/16, 1] or whose cumulative decay drops below 2^-60, and a final partial
-// block, run the plain step on the scan waves instead (y on the VALU, no
-// rescaling).  Checkpoints must fall on block starts (chunk a multiple of 32).
+// steps are done; Y: the state after the block is in LDS).  Blocks whose
+// decays leave [1/16, 1] or whose cumulative decay drops below 2^-60, and a
+// final partial block, run the plain step on the scan waves instead (y on
+// the VALU, no rescaling).  Checkpoints must fall on block starts (chunk a
+// multiple of 32).
 
 #include <type_traits>
 
@@ -44,6 +45,8 @@ constexpr int kTB = 32;                    // steps per block
 constexpr float kWMinF = 0.0625f;          // smallest decay of a rescaled block
 constexpr float kGMinF = 8.67361738e-19f;  // 2^-60: smallest cumulative decay
 constexpr unsigned kSpinMax = 1u << 20;    // bound on one helper wait (polls)
+constexpr int kNH = 8;                     // helper waves
+constexpr int kThreads = 64 * (4 + kNH);
 
 __device__ __forceinline__ f4 mfma(float a, float b, f4 c)
 {
@@ -98,7 +101,7 @@ struct FwdcArgs {
 };
 
 template <typename TIn>
-__global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
+__global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
 {
     constexpr int N = 64, R = 2, CC = 8, LPR = 8;
     __shared__ __align__(16) float slot[2][6][kTB * N];  // block inputs, by q & 1
@@ -172,81 +175,8 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
             if (cg < R) *base_row_t = val;
         };
 
-        // The read-out y of a rescaled block, on the matrix cores: tile tb
-        // holds steps 16 tb .. 16 tb + 15 (accumulator row 4 gq + i) of rows
-        // 16 wave .. 16 wave + 15 of S (accumulator column l16).
-        const bool want_y = p.y != nullptr;
-        const int l16 = lane & 15, gq = lane >> 4, qa = l16 >> 2, c3 = l16 & 3;
-        // rows 16 X + l16, columns 16 q4 + 4 gq .. + 3:  L1[q4] + 1024 X
-        int L1[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) L1[q4] = 64 * l16 + 16 * (q4 ^ qa) + 4 * (gq ^ c3);
-        // rows 16 U + 4 gq + r, column 16 wave + l16:  Lv[r] + 1024 U
-        int Lv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Lv[r] = 256 * gq + 64 * r + 16 * (wave ^ gq) + 4 * (qa ^ r) + c3;
-        // Gram tiles kt.rb and bt.rb of the next block, (u-block, t-block)
-        // = (0,0), (0,1), (1,1); read while the helpers leave them in place
-        f4 Pk[3], Pb[3];
-        auto read_grams = [&]() {
-#pragma unroll
-            for (int pos = 0; pos < 3; ++pos) {
-                Pk[pos] = *reinterpret_cast<const f4 *>(&gram[3 + pos][4 * lane]);
-                Pb[pos] = *reinterpret_cast<const f4 *>(&gram[6 + pos][4 * lane]);
-            }
-        };
-        // y_t = S0 rb_t + sum_{u<=t} v_u (kt_u . rb_t) + sa_u (bt_u . rb_t)
-        auto y_block = [&](int bb, int64_t t0) {
-            const float *rbv = slot[bb][vR], *vv = slot[bb][vV], *sav = sap[bb];
-            float4 sr[4], xr[2][4];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                sr[q4] = lds4(sS0 + 1024 * wave, L1[q4]);
-                xr[0][q4] = lds4(rbv, L1[q4]);
-                xr[1][q4] = lds4(rbv + 1024, L1[q4]);
-            }
-            float vb[2][4], sb[2][4];
-#pragma unroll
-            for (int ub = 0; ub < 2; ++ub)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    vb[ub][r] = vv[1024 * ub + Lv[r]];
-                    sb[ub][r] = sav[1024 * ub + Lv[r]];
-                }
-            f4 Y[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb) Y[tb] = mfma(xr[tb][q4].x, sr[q4].x, Y[tb]);
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb) Y[tb] = mfma(xr[tb][q4].y, sr[q4].y, Y[tb]);
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb) Y[tb] = mfma(xr[tb][q4].z, sr[q4].z, Y[tb]);
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb) Y[tb] = mfma(xr[tb][q4].w, sr[q4].w, Y[tb]);
-            }
-#pragma unroll
-            for (int ub = 0; ub < 2; ++ub)
-#pragma unroll
-                for (int tb = ub; tb < 2; ++tb) {
-                    const int pos = tb == 0 ? 0 : 1 + ub;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        Y[tb] = mfma(Pk[pos][r], vb[ub][r], Y[tb]);
-                        Y[tb] = mfma(Pb[pos][r], sb[ub][r], Y[tb]);
-                    }
-                }
-            float *dst = p.y + vbase + t0 * stride + 16 * wave + l16;
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dst[(16 * tb + 4 * gq + i) * stride] = Y[tb][i];
-        };
-
         put_state();
         __syncthreads();   // block 0 ready, S0 in LDS
-        read_grams();
-        __syncthreads();   // the helpers may now replace the Gram tiles
 
         for (int64_t q = 0; q < nblk; ++q) {
             const int bb = (int)(q & 1);
@@ -265,14 +195,13 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                     row8(Lb, s, o.bt);
                     o.c = *reinterpret_cast<const float2 *>(Lc + sw(s, row0));
                 };
-                // operands two steps ahead
-                Ops ops[3];
+                // operands one step ahead
+                Ops ops[2];
                 load_ops(0, ops[0]);
-                load_ops(1, ops[1]);
 #pragma unroll
                 for (int s = 0; s < kTB; ++s) {
-                    if (s + 2 < kTB) load_ops(s + 2, ops[(s + 2) % 3]);
-                    const Ops &o = ops[s % 3];
+                    if (s + 1 < kTB) load_ops(s + 1, ops[(s + 1) & 1]);
+                    const Ops &o = ops[s & 1];
                     float sa[R];
 #pragma unroll
                     for (int e = 0; e < R; ++e) {
@@ -290,7 +219,6 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                         for (int c = 0; c < CC; ++c) S[e][c] = fmaf(sa[e], o.bt[c], S[e][c]);
                     park(&SA[sw(s, row0 + cg)], sa);
                 }
-                if (want_y) y_block(bb, t0);
                 __syncthreads();   // X: steps done; sum v kt^T is in LDS
                 float gr[CC];
                 {
@@ -345,7 +273,6 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                 __syncthreads();   // X
             }
             put_state();           // the state before block q + 1
-            read_grams();          // (block q + 1's, computed during block q)
             __syncthreads();       // Y
         }
         if (p.sT) {
@@ -366,20 +293,22 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
     // offsets plus a constant, so that the helpers spend their issue slots
     // on loads, stores and MFMAs rather than on address arithmetic.
     const int l16 = lane & 15, g = lane >> 4, qa = l16 >> 2, c3 = l16 & 3;
+    const bool want_y = p.y != nullptr;
     const TIn *in_ptr[6];
 #pragma unroll
     for (int v = 0; v < 6; ++v) in_ptr[v] = p.in[v] + vbase;
+    float *const y_out = p.y ? p.y + vbase : nullptr;
     float *const sa_out = p.sa ? p.sa + vbase : nullptr;
     float *const ck_out = p.ckpt;
     const int chunk = p.chunk, nck = p.nck;
     float *const gbuf = &gram[0][0];   // g of the block being rescaled
 
-    // Wait until all four helper waves have arrived here.  Every helper wave
+    // Wait until all helper waves have arrived here.  Every helper wave
     // runs the same sequence of waits; the poll count is bounded so that a
     // broken sequence ends the kernel with wrong results instead of a hang.
     unsigned htarget = 0;
     auto hsync = [&]() {
-        htarget += 4;
+        htarget += kNH;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         if (lane == 0) __hip_atomic_fetch_add(&hcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         for (unsigned it = 0; it < kSpinMax; ++it) {
@@ -391,51 +320,48 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
 
     auto helper = [&](auto hw) {
         constexpr int h = decltype(hw)::value;
-        // y tiles of this wave: steps 16 tb .. 16 tb + 15, rows 16 (2 ih + m)
-        // .. + 15 for m = 0, 1 (lane: step 16 tb + 4 g + r, row .. + l16)
-        constexpr int tb = h & 1, ih = h >> 1;
+        // The y and c tile of this wave: steps 16 tb .. 16 tb + 15 of the
+        // block (lane: step 16 tb + 4 g + r), rows 16 ib .. 16 ib + 15 (lane:
+        // row 16 ib + l16).  Its part of sum v kt^T: rows 16 ib .., column
+        // tiles 2 tb and 2 tb + 1.
+        constexpr int tb = h & 1, ib = h >> 1;
 
         // ---- lane offsets (floats) into the swizzled [rows][64] arrays:
         //   rows 16 X + l16, columns 16 q4 + 4 g .. + 3    L1[q4] + 1024 X
-        //   rows 16 U + 4 g + r, column 16 (2 ih + m) + l16    L2[m][r] + 1024 U
+        //   rows 16 U + 4 g + r, column 16 ib + l16         L2[r] + 1024 U
         //   rows 4 k + g, column 16 I + l16    L3 + 256 k + 16 (I ^ (k & 3))
-        int L1[4], L2[2][4];
+        int L1[4], L2[4];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) L1[q4] = 64 * l16 + 16 * (q4 ^ qa) + 4 * (g ^ c3);
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                L2[m][r] = 256 * g + 64 * r + 16 * ((2 * ih + m) ^ g) + 4 * (qa ^ r) + c3;
+        for (int r = 0; r < 4; ++r) L2[r] = 256 * g + 64 * r + 16 * (ib ^ g) + 4 * (qa ^ r) + c3;
         const int L3 = 64 * g + 4 * (qa ^ g) + c3;
         // sum v kt^T, stored transposed: row j = 16 jt + l16, columns
-        // 16 h + 4 g .. + 3
-        const int Lt = 64 * l16 + 4 * ((4 * h + g) ^ l16);
-        // rescaling by rows: step tr, columns 8 cq + 4 m .. + 3
-        const int tr = 8 * h + (lane >> 3), cq = lane & 7;
-        int Lr[2], Lp[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            Lr[m] = 64 * tr + 4 * ((2 * cq + m) ^ (tr & 15));
-            Lp[m] = tr > 0 ? 64 * (tr - 1) + 4 * ((2 * cq + m) ^ ((tr - 1) & 15)) : 0;
-        }
-        // tape and checkpoints: rows 4 h + 16 k + g, columns 4 l16 .. + 3
-        const int Lq = 64 * g + 4 * (l16 ^ (4 * h + g));
+        // 16 ib + 4 g .. + 3
+        const int Lt = 64 * l16 + 4 * ((4 * ib + g) ^ l16);
+        // rescaling by rows: step tr, columns 4 cq .. + 3
+        const int tr = 4 * h + (lane >> 4), cq = lane & 15;
+        const int Lr = 64 * tr + 4 * (cq ^ (tr & 15));
+        const int Lp = tr > 0 ? 64 * (tr - 1) + 4 * (cq ^ ((tr - 1) & 15)) : 0;
+        // tape: row 4 h + g, columns 4 l16 .. + 3 (from the row 16 (h / 4))
+        const int Lq = 64 * g + 4 * (l16 ^ (4 * (h & 3) + g));
         // global offsets (elements)
+        const int Ly = 4 * g * (int)stride + l16;   // y: step 4 g, row l16
         const int Ls = g * (int)stride + 4 * l16;   // tape: step g, column 4 l16
         int Ld[4];                                  // staging: step g, swizzled column
 #pragma unroll
         for (int u = 0; u < 4; ++u) Ld[u] = g * (int)stride + 4 * (l16 ^ (4 * u + g));
 
         // ---- staging of block blk into slot[b]: units of 1 KB (4 steps of
-        // one input), 12 per helper wave; fp32 by direct HBM -> LDS copies
+        // one input), 6 per helper wave; fp32 by direct HBM -> LDS copies
         // (lane l of a unit lands at float 4 l: step 4 u + l / 16, swizzled
         // column group l % 16), bf16 through registers (widened)
+        constexpr int kU = 48 / kNH;
         constexpr bool kDma = std::is_same<TIn, float>::value;
         using Raw = typename InQuad<TIn>::raw;
-        Raw pre[12];
+        Raw pre[kU];
         auto stage_unit = [&](int64_t t0, int b, int k) {
-            const int unit = 12 * h + k, v = unit >> 3, u = unit & 7;
+            const int unit = kU * h + k, v = unit >> 3, u = unit & 7;
             const TIn *base = in_ptr[v] + (t0 + 4 * u) * stride;
             if constexpr (kDma) {
                 const unsigned lds = (unsigned)(uintptr_t)(
@@ -450,11 +376,11 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
             const int64_t t0 = blk * kTB;
             if (nst == kTB) {   // a full block: no per-lane condition
 #pragma unroll
-                for (int k = 0; k < 12; ++k) stage_unit(t0, b, k);
+                for (int k = 0; k < kU; ++k) stage_unit(t0, b, k);
             } else {
 #pragma unroll
-                for (int k = 0; k < 12; ++k)
-                    if (4 * ((12 * h + k) & 7) + g < nst) stage_unit(t0, b, k);
+                for (int k = 0; k < kU; ++k)
+                    if (4 * ((kU * h + k) & 7) + g < nst) stage_unit(t0, b, k);
             }
         };
         auto stage_land = [&](int64_t blk, int b) {
@@ -463,8 +389,8 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
             } else {
                 const int nst = steps_of(blk);
 #pragma unroll
-                for (int k = 0; k < 12; ++k) {
-                    const int unit = 12 * h + k, v = unit >> 3, u = unit & 7;
+                for (int k = 0; k < kU; ++k) {
+                    const int unit = kU * h + k, v = unit >> 3, u = unit & 7;
                     if (nst == kTB || 4 * u + g < nst)
                         put4(&slot[b][v][u * 256], 4 * lane, InQuad<TIn>::f32(pre[k]));
                 }
@@ -472,60 +398,49 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
         };
 
         // ---- rescaling of the staged block in slot[b], in place.  First g,
-        // per column: lane (l16, g) owns column 16 h + l16 and steps 4 u + g,
-        // u = 0 .. 7 (prefix products over each group of four steps by lane
-        // exchanges); g goes to the Gram area, free until the Gram tiles.
-        // Then, if every column is in range, r, a, k, b are rescaled by rows.
-        // Returns whether the block is rescaled (the same in every helper).
+        // per column, by helpers 0-3: lane (l16, g) owns column 16 h + l16
+        // and steps 4 u + g, u = 0 .. 7 (prefix products over each group of
+        // four steps by lane exchanges); g goes to the Gram area, free until
+        // the Gram tiles.  Then, if every column is in range, r, a, k, b are
+        // rescaled by rows (four rows per helper).  Returns whether the block
+        // is rescaled (the same in every helper).
         auto prep = [&](int b, int nstn) -> bool {
             float *const sb = &slot[b][0][0];
-            bool ok = nstn == kTB;
-            if (ok) {
-                float wv[8];
+            if constexpr (h < 4) {
+                bool ok = nstn == kTB;
+                if (ok) {
+                    float wv[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) wv[u] = sb[vW * 2048 + L3 + 256 * u + 16 * (h ^ (u & 3))];
-                float G = 1.f;   // product over the steps before 4 u
+                    for (int u = 0; u < 8; ++u) wv[u] = sb[vW * 2048 + L3 + 256 * u + 16 * (h ^ (u & 3))];
+                    float G = 1.f;   // product over the steps before 4 u
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float x = wv[u], x1 = xor16(x, g);
-                    const float pre2 = (g & 1) ? x1 * x : x;   // within the pair
-                    const float pair = (g & 1) ? pre2 : x * x1;
-                    const float other = xor32(pair, g);        // the other pair
-                    const float gt = G * ((g & 2) ? other * pre2 : pre2);
-                    G *= pair * other;
-                    gbuf[L3 + 256 * u + 16 * (h ^ (u & 3))] = gt;
-                    ok = ok && x >= kWMinF && x <= 1.f && gt >= kGMinF;
+                    for (int u = 0; u < 8; ++u) {
+                        const float x = wv[u], x1 = xor16(x, g);
+                        const float pre2 = (g & 1) ? x1 * x : x;   // within the pair
+                        const float pair = (g & 1) ? pre2 : x * x1;
+                        const float other = xor32(pair, g);        // the other pair
+                        const float gt = G * ((g & 2) ? other * pre2 : pre2);
+                        G *= pair * other;
+                        gbuf[L3 + 256 * u + 16 * (h ^ (u & 3))] = gt;
+                        ok = ok && x >= kWMinF && x <= 1.f && gt >= kGMinF;
+                    }
                 }
+                if (!ok) hbad[b] = 1;   // every writer stores 1
             }
-            if (!ok) hbad[b] = 1;   // every writer stores 1
             hsync();
-            const bool fast = __builtin_amdgcn_readfirstlane(hbad[b]) == 0;
+            const bool fast = nstn == kTB && __builtin_amdgcn_readfirstlane(hbad[b]) == 0;
             if (fast) {
-                float4 gt[2], gp[2], x[4][2];
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    gt[m] = lds4(gbuf, Lr[m]);
-                    gp[m] = lds4(gbuf, Lp[m]);
-                    if (h == 0 && tr == 0) gp[m] = make_float4(1.f, 1.f, 1.f, 1.f);
-                    x[0][m] = lds4(sb + vR * 2048, Lr[m]);
-                    x[1][m] = lds4(sb + vA * 2048, Lr[m]);
-                    x[2][m] = lds4(sb + vK * 2048, Lr[m]);
-                    x[3][m] = lds4(sb + vB * 2048, Lr[m]);
-                }
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const float4 iv = make_float4(__builtin_amdgcn_rcpf(gt[m].x), __builtin_amdgcn_rcpf(gt[m].y),
-                                                  __builtin_amdgcn_rcpf(gt[m].z), __builtin_amdgcn_rcpf(gt[m].w));
-                    put4(sb + vR * 2048, Lr[m], make_float4(x[0][m].x * gt[m].x, x[0][m].y * gt[m].y,
-                                                            x[0][m].z * gt[m].z, x[0][m].w * gt[m].w));
-                    put4(sb + vA * 2048, Lr[m], make_float4(x[1][m].x * gp[m].x, x[1][m].y * gp[m].y,
-                                                            x[1][m].z * gp[m].z, x[1][m].w * gp[m].w));
-                    put4(sb + vK * 2048, Lr[m], make_float4(x[2][m].x * iv.x, x[2][m].y * iv.y,
-                                                            x[2][m].z * iv.z, x[2][m].w * iv.w));
-                    put4(sb + vB * 2048, Lr[m], make_float4(x[3][m].x * iv.x, x[3][m].y * iv.y,
-                                                            x[3][m].z * iv.z, x[3][m].w * iv.w));
-                    if (h == 3 && tr == kTB - 1) put4(g31[b], 8 * cq + 4 * m, gt[m]);
-                }
+                float4 gt = lds4(gbuf, Lr), gp = lds4(gbuf, Lp);
+                if (h == 0 && tr == 0) gp = make_float4(1.f, 1.f, 1.f, 1.f);
+                const float4 x0 = lds4(sb + vR * 2048, Lr), x1 = lds4(sb + vA * 2048, Lr);
+                const float4 x2 = lds4(sb + vK * 2048, Lr), x3 = lds4(sb + vB * 2048, Lr);
+                const float4 iv = make_float4(__builtin_amdgcn_rcpf(gt.x), __builtin_amdgcn_rcpf(gt.y),
+                                              __builtin_amdgcn_rcpf(gt.z), __builtin_amdgcn_rcpf(gt.w));
+                put4(sb + vR * 2048, Lr, make_float4(x0.x * gt.x, x0.y * gt.y, x0.z * gt.z, x0.w * gt.w));
+                put4(sb + vA * 2048, Lr, make_float4(x1.x * gp.x, x1.y * gp.y, x1.z * gp.z, x1.w * gp.w));
+                put4(sb + vK * 2048, Lr, make_float4(x2.x * iv.x, x2.y * iv.y, x2.z * iv.z, x2.w * iv.w));
+                put4(sb + vB * 2048, Lr, make_float4(x3.x * iv.x, x3.y * iv.y, x3.z * iv.z, x3.w * iv.w));
+                if (h == kNH - 1 && tr == kTB - 1) put4(g31[b], 4 * cq, gt);
             }
             return fast;
         };
@@ -533,20 +448,26 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
         // ---- Gram tile n: kind n / 3 (0: kt . ab with u < t, 1: kt . rb,
         // 2: bt . rb, both u <= t), position n % 3 = (u-block, t-block)
         // (0,0), (0,1), (1,1); D[u][t] in the accumulator layout, stored
-        // lane-linear.  Wave h computes tiles h and h + 4 (and 8 for h = 0).
-        auto gram_load = [&](const float *sb, auto nc, float4 (&xq)[4], float4 (&zq)[4]) {
+        // lane-linear.  Wave h computes tile h; wave 4 also tile 8.
+        auto gram_tile = [&](const float *sb, auto nc) {
             constexpr int n = decltype(nc)::value, kind = n / 3, pos = n % 3;
             constexpr int ub = pos == 2 ? 1 : 0, tn = pos == 0 ? 0 : 1;
             constexpr int xo = (kind == 2 ? vB : vK) * 2048 + 1024 * ub;
             constexpr int zo = (kind == 0 ? vA : vR) * 2048 + 1024 * tn;
+            float4 xq[4], zq[4];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 xq[q4] = lds4(sb + xo, L1[q4]);
                 zq[q4] = lds4(sb + zo, L1[q4]);
             }
-        };
-        auto gram_store = [&](auto nc, f4 acc) {
-            constexpr int n = decltype(nc)::value, kind = n / 3, pos = n % 3;
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                acc = mfma(xq[q4].x, zq[q4].x, acc);
+                acc = mfma(xq[q4].y, zq[q4].y, acc);
+                acc = mfma(xq[q4].z, zq[q4].z, acc);
+                acc = mfma(xq[q4].w, zq[q4].w, acc);
+            }
             if constexpr (pos != 1) {   // a diagonal tile
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -557,71 +478,72 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
             *reinterpret_cast<f4 *>(&gram[n][4 * lane]) = acc;
         };
         auto grams = [&](const float *sb) {
-            using N0 = std::integral_constant<int, h>;
-            using N1 = std::integral_constant<int, h + 4>;
-            float4 xa[4], za[4], xb[4], zb[4];
-            gram_load(sb, N0{}, xa, za);
-            gram_load(sb, N1{}, xb, zb);
-            f4 a = {0.f, 0.f, 0.f, 0.f}, c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                a = mfma(xa[q4].x, za[q4].x, a);
-                c = mfma(xb[q4].x, zb[q4].x, c);
-                a = mfma(xa[q4].y, za[q4].y, a);
-                c = mfma(xb[q4].y, zb[q4].y, c);
-                a = mfma(xa[q4].z, za[q4].z, a);
-                c = mfma(xb[q4].z, zb[q4].z, c);
-                a = mfma(xa[q4].w, za[q4].w, a);
-                c = mfma(xb[q4].w, zb[q4].w, c);
-            }
-            gram_store(N0{}, a);
-            gram_store(N1{}, c);
-            if constexpr (h == 0) {
-                using N2 = std::integral_constant<int, 8>;
-                gram_load(sb, N2{}, xa, za);
-                f4 e = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    e = mfma(xa[q4].x, za[q4].x, e);
-                    e = mfma(xa[q4].y, za[q4].y, e);
-                    e = mfma(xa[q4].z, za[q4].z, e);
-                    e = mfma(xa[q4].w, za[q4].w, e);
-                }
-                gram_store(N2{}, e);
-            }
+            gram_tile(sb, std::integral_constant<int, h>{});
+            if constexpr (h == 4) gram_tile(sb, std::integral_constant<int, 8>{});
         };
         auto gram_get = [&](int kind, int ub) -> f4 {
             const int pos = tb == 0 ? 0 : 1 + ub;
             return *reinterpret_cast<const f4 *>(&gram[3 * kind + pos][4 * lane]);
         };
 
-        f4 VK[4];
-        bool fastB = false;   // block q
+        f4 Y, Yv, VK[2], PbA[2], PbB[2], PbC[2];
+        bool fastA = false, fastB = false;   // blocks q - 1 and q
+        Y = Yv = VK[0] = VK[1] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) VK[jt] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < 2; ++m) PbA[m] = PbB[m] = PbC[m] = f4{0.f, 0.f, 0.f, 0.f};
 
+        // y of a block from its S0: Y = Yv + S0 rb_t
+        auto y_from_s0 = [&](int b) {
+            const float *xs = &slot[b][vR][1024 * tb];
+            float4 xr[4], sr[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                xr[q4] = lds4(xs, L1[q4]);
+                sr[q4] = lds4(sS0 + 1024 * ib, L1[q4]);
+            }
+            Y = Yv;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                Y = mfma(xr[q4].x, sr[q4].x, Y);
+                Y = mfma(xr[q4].y, sr[q4].y, Y);
+                Y = mfma(xr[q4].z, sr[q4].z, Y);
+                Y = mfma(xr[q4].w, sr[q4].w, Y);
+            }
+        };
+        // the sa terms of the block whose sa is in sap[b]:
+        // Y += sum_u (bt_u . rb_t) sa_u
+        auto y_from_sa = [&](int b) {
+            float sv[2][4];
+#pragma unroll
+            for (int ub = 0; ub <= tb; ++ub)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sv[ub][r] = sap[b][1024 * ub + L2[r]];
+#pragma unroll
+            for (int ub = 0; ub <= tb; ++ub)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Y = mfma(PbA[ub][r], sv[ub][r], Y);
+        };
+        auto y_store = [&](int64_t t0) {
+            float *dst = y_out + (t0 + 16 * tb) * stride + 16 * ib;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[Ly + r * stride] = Y[r];
+        };
         auto tape_out = [&](int64_t blk, int b) {
             if (!sa_out) return;
             const int nst = steps_of(blk);
             float *dst = sa_out + (blk * kTB + 4 * h) * stride;
-            if (nst == kTB) {
-#pragma unroll
-                for (int k = 0; k < 2; ++k)
-                    *reinterpret_cast<float4 *>(dst + 16 * k * stride + Ls) = lds4(sap[b] + 256 * h + 1024 * k, Lq);
-            } else {
-#pragma unroll
-                for (int k = 0; k < 2; ++k)
-                    if (4 * h + 16 * k + g < nst)
-                        *reinterpret_cast<float4 *>(dst + 16 * k * stride + Ls) = lds4(sap[b] + 256 * h + 1024 * k, Lq);
-            }
+            if (nst == kTB || 4 * h + g < nst)
+                *reinterpret_cast<float4 *>(dst + Ls) = lds4(sap[b] + 256 * (h & 3) + 1024 * (h >> 2), Lq);
         };
         auto ckpt_out = [&](int64_t blk) {
             const int64_t t = blk * kTB;
             if (!ck_out || t % chunk != 0) return;
-            float *dst = ck_out + (bh * nck + t / chunk) * N * N + 256 * h;
+            float *dst = ck_out + (bh * nck + t / chunk) * N * N;
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                *reinterpret_cast<float4 *>(dst + 1024 * k + 64 * g + 4 * l16) = lds4(sS0 + 256 * h + 1024 * k, Lq);
+            for (int k = 0; k < 2; ++k) {
+                const int row = 8 * h + 4 * k + g;
+                *reinterpret_cast<float4 *>(dst + 64 * row + 4 * l16) = lds4(sS0, sw(row, 4 * l16));
+            }
         };
 
         // Phase q (q = -1 before the first block): the scan waves run block
@@ -633,15 +555,24 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
             if (q >= 0 && fastB) {
                 // sum_u v_u kt_u^T of block q, for the end of its steps
 #pragma unroll
-                for (int jt = 0; jt < 4; ++jt)
-                    put4(vkt + 1024 * jt, Lt, make_float4(VK[jt][0], VK[jt][1], VK[jt][2], VK[jt][3]));
+                for (int m = 0; m < 2; ++m)
+                    put4(vkt + 1024 * (2 * tb + m), Lt, make_float4(VK[m][0], VK[m][1], VK[m][2], VK[m][3]));
             }
             if (next) {
                 stage_issue(q + 1, bn);
                 if (h == 0 && lane == 0) hbad[bn] = 0;
             }
-            if (q >= 1) tape_out(q - 1, bn);
-            if (q >= 0) ckpt_out(q);
+            if (q >= 1) {
+                if (fastA && want_y) {
+                    y_from_sa(bn);
+                    y_store((q - 1) * kTB);
+                }
+                tape_out(q - 1, bn);
+            }
+            if (q >= 0) {
+                ckpt_out(q);
+                if (fastB && want_y) y_from_s0(bb);
+            }
             bool fastC = false;
             if (next) {
                 stage_land(q + 1, bn);
@@ -653,46 +584,46 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                     hsync();   // block q + 1 rescaled
                     grams(sb);
                     hsync();   // Gram tiles in LDS
-                    f4 Mk[2];
+                    f4 Mk[2], Pk[2];
 #pragma unroll
-                    for (int ub = 0; ub <= tb; ++ub) Mk[ub] = gram_get(0, ub);
-                    // c, into the slot of w
-                    float vb[2][2][4];
+                    for (int ub = 0; ub <= tb; ++ub) {
+                        Mk[ub] = gram_get(0, ub);
+                        Pk[ub] = gram_get(1, ub);
+                        PbC[ub] = gram_get(2, ub);
+                    }
+                    // c (into the slot of w) and the v terms of y
+                    float vb[2][4];
 #pragma unroll
                     for (int ub = 0; ub <= tb; ++ub)
 #pragma unroll
-                        for (int m = 0; m < 2; ++m)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) vb[ub][m][r] = sb[vV * 2048 + 1024 * ub + L2[m][r]];
-                    // rows 16 h .. 16 h + 15 of sum_u v_u kt_u^T: operands
-                    float va[8], kb[8][4];
+                        for (int r = 0; r < 4; ++r) vb[ub][r] = sb[vV * 2048 + 1024 * ub + L2[r]];
+                    // rows 16 ib .. 16 ib + 15 of sum_u v_u kt_u^T, column
+                    // tiles 2 tb, 2 tb + 1: operands
+                    float va[8], kb[8][2];
 #pragma unroll
                     for (int kk = 0; kk < 8; ++kk) {
-                        va[kk] = sb[vV * 2048 + L3 + 256 * kk + 16 * (h ^ (kk & 3))];
+                        va[kk] = sb[vV * 2048 + L3 + 256 * kk + 16 * (ib ^ (kk & 3))];
 #pragma unroll
-                        for (int jt = 0; jt < 4; ++jt) kb[kk][jt] = sb[vK * 2048 + L3 + 256 * kk + 16 * (jt ^ (kk & 3))];
+                        for (int m = 0; m < 2; ++m)
+                            kb[kk][m] = sb[vK * 2048 + L3 + 256 * kk + 16 * ((2 * tb + m) ^ (kk & 3))];
                     }
-                    f4 cacc[2];
-#pragma unroll
-                    for (int m = 0; m < 2; ++m) cacc[m] = f4{0.f, 0.f, 0.f, 0.f};
+                    f4 cacc = {0.f, 0.f, 0.f, 0.f}, yacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ub = 0; ub <= tb; ++ub)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-#pragma unroll
-                            for (int m = 0; m < 2; ++m) cacc[m] = mfma(Mk[ub][r], vb[ub][m][r], cacc[m]);
-#pragma unroll
-                    for (int jt = 0; jt < 4; ++jt) VK[jt] = f4{0.f, 0.f, 0.f, 0.f};
+                        for (int r = 0; r < 4; ++r) {
+                            cacc = mfma(Mk[ub][r], vb[ub][r], cacc);
+                            yacc = mfma(Pk[ub][r], vb[ub][r], yacc);
+                        }
+                    VK[0] = VK[1] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-                        for (int jt = 0; jt < 4; ++jt) VK[jt] = mfma(va[kk], kb[kk][jt], VK[jt]);
+                        for (int m = 0; m < 2; ++m) VK[m] = mfma(va[kk], kb[kk][m], VK[m]);
+                    Yv = yacc;
+                    float *cs = &slot[bn][vW][1024 * tb];
 #pragma unroll
-                    for (int m = 0; m < 2; ++m) {
-                        float *cs = &slot[bn][vW][1024 * tb];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) cs[L2[m][r]] = cacc[m][r];
-                    }
+                    for (int r = 0; r < 4; ++r) cs[L2[r]] = cacc[r];
                 }
             }
             if (q >= 0) {
@@ -700,18 +631,34 @@ __global__ void __launch_bounds__(512) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                 __syncthreads();   // Y: the state after block q in LDS
             } else {
                 __syncthreads();   // block 0 ready, S0 in LDS
-                __syncthreads();   // the scan waves hold block 0's Gram tiles
             }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                PbA[m] = PbB[m];
+                PbB[m] = PbC[m];
+            }
+            fastA = fastB;
             fastB = fastC;
         }
-        // the last block's tape
-        if (nblk > 0) tape_out(nblk - 1, (int)((nblk - 1) & 1));
+        // the last block's sa terms of y and its tape
+        if (nblk > 0) {
+            const int bl = (int)((nblk - 1) & 1);
+            if (fastA && want_y) {
+                y_from_sa(bl);
+                y_store((nblk - 1) * kTB);
+            }
+            tape_out(nblk - 1, bl);
+        }
     };
     switch (wave) {
     case 4: helper(std::integral_constant<int, 0>{}); break;
     case 5: helper(std::integral_constant<int, 1>{}); break;
     case 6: helper(std::integral_constant<int, 2>{}); break;
-    default: helper(std::integral_constant<int, 3>{}); break;
+    case 7: helper(std::integral_constant<int, 3>{}); break;
+    case 8: helper(std::integral_constant<int, 4>{}); break;
+    case 9: helper(std::integral_constant<int, 5>{}); break;
+    case 10: helper(std::integral_constant<int, 6>{}); break;
+    default: helper(std::integral_constant<int, 7>{}); break;
     }
 }
 
@@ -729,7 +676,7 @@ hipError_t launch_fwdc_t(const FwdLaunch &a, hipStream_t stream)
     p.H = a.H;
     p.chunk = a.chunk;
     p.nck = (int)((a.T + a.chunk - 1) / a.chunk);
-    hipLaunchKernelGGL((wkv7_fwdc_kernel<TIn>), dim3((unsigned)(a.B * a.H)), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((wkv7_fwdc_kernel<TIn>), dim3((unsigned)(a.B * a.H)), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
