@@ -1,5 +1,5 @@
-// WKV7 forward for N = 64: a serial scan on four waves beside four waves that
-// prepare its inputs and compute its outputs on the matrix cores.
+// WKV7 forward for N = 64: a serial scan on four waves beside eight waves
+// that prepare its inputs and compute its outputs on the matrix cores.
 //
 // The recurrence is rx_wkv7_forward_seq on the Foundry "rwkvx/rx_pretrain.c"
 // page: sa = S a;  S <- S diag(w) + v k^T + sa b^T;  y = S r.  Per block of

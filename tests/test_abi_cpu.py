@@ -95,6 +95,12 @@ def test_backward_validation():
     assert _bwd(_shape(N=16, algo=2)) == _lib.WKV7_ERR_UNSUPPORTED
     assert _bwd(_shape(chunk=32, algo=2)) == _lib.WKV7_ERR_UNSUPPORTED
     assert _bwd(_shape(chunk=128, algo=2)) == _lib.WKV7_ERR_UNSUPPORTED
+    # ... and one batch row of a vector tensor below 2^31 bytes (32-bit
+    # offsets): T*H*64*4 < 2^31
+    edge = (1 << 31) // (64 * 4)                        # T*H at the limit
+    assert _bwd(_shape(B=1, T=edge, H=1, algo=2)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert _bwd(_shape(B=1, T=edge // 64, H=64, algo=2)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert _bwd(_shape(B=1, T=edge - 1, H=1, algo=2)) == _lib.WKV7_ERR_WORKSPACE
     # workspace missing / too small / misaligned
     assert _bwd(sh) == _lib.WKV7_ERR_WORKSPACE
     need = _lib.lib().wkv7_backward_workspace_bytes(ctypes.byref(sh), 0)
