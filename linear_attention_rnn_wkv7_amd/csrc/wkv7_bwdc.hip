@@ -319,25 +319,109 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                   dst_[q] + blk * 256);
         }
     };
+    // fp32: the cumulative decay of the next chunk is formed in registers
+    // during the current one (w read straight from global memory) and put
+    // into sG once the current chunk is done with it, so that the next
+    // chunk's prologue is a single pass.  Wave w takes columns 8 w ..
+    // 8 w + 7; lane (seg, cw) the steps 8 seg .. 8 seg + 7 of column 8 w + cw.
+    float gn[8];   // w of the next chunk, then its cumulative decay
+    bool gok = true;
+    auto load_w = [&](int cc) {
+        const int cw = ltid & 7, seg = (ltid >> 3) & 7, j = (ltid >> 6) * 8 + cw;
+        const BufRsrc rw = raw_buffer(p.w + vbase, vext * sizeof(TIn) / 4);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            gn[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                rw, (int)((((uint32_t)cc * 64 + 8 * seg + u) * ustride + j) * 4), 0, 0));
+    };
+    auto scan_w = [&](int Lcc) {
+        const int seg = (ltid >> 3) & 7, ln = ltid & 63;
+        float pr = 1.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (8 * seg + u >= Lcc) gn[u] = 1.f;   // past the end of the sequence
+            pr *= gn[u];
+        }
+        float inc = pr;   // product over segments 0 .. seg
+#pragma unroll
+        for (int d = 1; d < 8; d *= 2) {
+            const float o = __builtin_bit_cast(
+                float, __builtin_amdgcn_ds_bpermute(4 * ((ln - 8 * d) & 63), __builtin_bit_cast(int, inc)));
+            inc = seg >= d ? inc * o : inc;
+        }
+        const float before = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute(4 * ((ln - 8) & 63), __builtin_bit_cast(int, inc)));
+        float pre_ = seg >= 1 ? before : 1.f;
+        bool ok = true;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float wv = gn[u];
+            pre_ *= wv;
+            ok = ok && wv >= kWMin && wv <= 1.f && pre_ >= kGMin;
+            gn[u] = pre_;
+        }
+        gok = ok;
+    };
+    auto store_g = [&]() {
+        const int cw = ltid & 7, seg = (ltid >> 3) & 7, j = (ltid >> 6) * 8 + cw;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sG[sw(seg * 8 + u, j)] = gn[u];
+        if (!gok) sBad = 1;   // every writer stores 1
+    };
     {
         const int cl = nck - 1, Ll = chunk_len(cl);
 #pragma unroll
-        for (int q = 0; q < 7; ++q) issue_regs(cl, q);
+        for (int q = 0; q < 7; ++q)
+            if (!kDma || q != 1) issue_regs(cl, q);
         issue_s0(cl);
+        if constexpr (kDma) {
+            // r, a, b, v raw into LDS; k and dy stay in registers for the
+            // chunk's prologue; the decay goes to sG
+            load_w(cl);
 #pragma unroll
-        for (int q = 0; q < 7; ++q) commit_regs(Ll, q);
+            for (int q = 0; q < 7; ++q)
+                if (q != 1 && q != 2 && q != 6) commit_regs(Ll, q);
+            scan_w(Ll);
+            store_g();
+        } else {
+#pragma unroll
+            for (int q = 0; q < 7; ++q) commit_regs(Ll, q);
+        }
     }
 
     for (int c = nck - 1; c >= 0; --c) {
         const int64_t t0 = (int64_t)c * 64;
         const int Lc = chunk_len(c);
 
+        if constexpr (kDma) {
+            // ---- prologue in one pass: g is in sG and r, a, b, v in their
+            // arrays (published by the previous barrier); k and dy come from
+            // registers, k scaled on the way in.  rb = r g, ab = a g_prev,
+            // kt = k / g, bt = b / g; Hb = H g_63
+            __syncthreads();
+            refresh();
+            commit_regs(Lc, 6);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
+                const int o = sw(t, j4);
+                const float4 gm = lds4(sG, o);
+                const float4 gp = t > 0 ? lds4(sG, sw(t - 1, j4)) : make_float4(1.f, 1.f, 1.f, 1.f);
+                const float4 inv = make_float4(1.f / gm.x, 1.f / gm.y, 1.f / gm.z, 1.f / gm.w);
+                const float4 kx = t < Lc ? InQuad<TIn>::f32(pre[2][m]) : make_float4(0.f, 0.f, 0.f, 0.f);
+                put4(sK, o, make_float4(kx.x * inv.x, kx.y * inv.y, kx.z * inv.z, kx.w * inv.w));
+                float4 x = lds4(sR, o);
+                put4(sR, o, make_float4(x.x * gm.x, x.y * gm.y, x.z * gm.z, x.w * gm.w));
+                x = lds4(sA, o);
+                put4(sA, o, make_float4(x.x * gp.x, x.y * gp.y, x.z * gp.z, x.w * gp.w));
+                x = lds4(sB, o);
+                put4(sB, o, make_float4(x.x * inv.x, x.y * inv.y, x.z * inv.z, x.w * inv.w));
+            }
+        } else {
         // ---- inputs of the chunk into LDS (the last chunk is there already)
         if (c != nck - 1) {
 #pragma unroll
-            for (int q = 0; q < 7; ++q)
-                if (!kDma || q == 2 || q == 6) commit_regs(64, q);
-            if (kDma) wait_dma();
+            for (int q = 0; q < 7; ++q) commit_regs(64, q);
         }
         __syncthreads();
         refresh();
@@ -376,7 +460,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         __syncthreads();
         refresh();
 
-        // ---- rb = r g, ab = a g_prev, kt = k / g, bt = b / g; Hb = H g_63
+        // ---- rb = r g, ab = a g_prev, kt = k / g, bt = b / g
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
@@ -393,6 +477,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             x = lds4(sB, o);
             put4(sB, o, make_float4(x.x * inv.x, x.y * inv.y, x.z * inv.z, x.w * inv.w));
         }
+        }   // bf16 prologue
         {
             const float g63 = sG[sw(63, jw)];
 #pragma unroll
@@ -403,6 +488,8 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         }
         __syncthreads();
         refresh();
+        // the next chunk's decay factors, read now, formed during this chunk
+        if (kDma && c > 0) load_w(c - 1);
         // Hb column jw (rows 16 g + s) and row jw (columns 16 g + s): the B
         // operands of its phase-2 products
         float hB[16], hR[16];
@@ -790,9 +877,11 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             // next chunk: r, w, a, b straight into their (now free) arrays
             if (kDma && c > 0) {
                 issue_dma(c - 1, 0);
-                issue_dma(c - 1, 1);
                 issue_dma(c - 1, 3);
                 issue_dma(c - 1, 4);
+                // sG is done with: the next chunk's cumulative decay
+                scan_w(64);
+                store_g();
             }
             sched_fence();
 
@@ -828,6 +917,8 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                     const int t = 16 * TB[lt] + 4 * g + i;
                     bstore(odv, ooff(t), XV[lt][i]);
                 }
+            // the next chunk's copies land before the barrier that publishes them
+            if (kDma && c > 0) wait_dma();
             __syncthreads();
             refresh();
         };
