@@ -383,6 +383,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                 if (q != 1 && q != 2 && q != 6) commit_regs(Ll, q);
             scan_w(Ll);
             store_g();
+            __syncthreads();   // (later chunks: the barrier ending the previous one)
         } else {
 #pragma unroll
             for (int q = 0; q < 7; ++q) commit_regs(Ll, q);
@@ -398,7 +399,6 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             // arrays (published by the previous barrier); k and dy come from
             // registers, k scaled on the way in.  rb = r g, ab = a g_prev,
             // kt = k / g, bt = b / g; Hb = H g_63
-            __syncthreads();
             refresh();
             commit_regs(Lc, 6);
 #pragma unroll
