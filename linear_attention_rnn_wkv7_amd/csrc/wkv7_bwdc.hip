@@ -399,23 +399,34 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             // arrays (published by the previous barrier); k and dy come from
             // registers, k scaled on the way in.  rb = r g, ab = a g_prev,
             // kt = k / g, bt = b / g; Hb = H g_63
+            // Every read is issued before the first write, and the step
+            // before t = 0 (decay 1) is a select, not a branch.
             refresh();
+            float4 gm[2], gp[2], xr[2], xa[2], xb[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
+                const int o = sw(t, j4);
+                gm[m] = lds4(sG, o);
+                gp[m] = lds4(sG, sw(t > 0 ? t - 1 : 0, j4));
+                xr[m] = lds4(sR, o);
+                xa[m] = lds4(sA, o);
+                xb[m] = lds4(sB, o);
+            }
             commit_regs(Lc, 6);
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
                 const int o = sw(t, j4);
-                const float4 gm = lds4(sG, o);
-                const float4 gp = t > 0 ? lds4(sG, sw(t - 1, j4)) : make_float4(1.f, 1.f, 1.f, 1.f);
-                const float4 inv = make_float4(1.f / gm.x, 1.f / gm.y, 1.f / gm.z, 1.f / gm.w);
+                const float4 gq = gm[m];
+                const float4 gv = t > 0 ? gp[m] : make_float4(1.f, 1.f, 1.f, 1.f);
+                const float4 inv = make_float4(__builtin_amdgcn_rcpf(gq.x), __builtin_amdgcn_rcpf(gq.y),
+                                               __builtin_amdgcn_rcpf(gq.z), __builtin_amdgcn_rcpf(gq.w));
                 const float4 kx = t < Lc ? InQuad<TIn>::f32(pre[2][m]) : make_float4(0.f, 0.f, 0.f, 0.f);
                 put4(sK, o, make_float4(kx.x * inv.x, kx.y * inv.y, kx.z * inv.z, kx.w * inv.w));
-                float4 x = lds4(sR, o);
-                put4(sR, o, make_float4(x.x * gm.x, x.y * gm.y, x.z * gm.z, x.w * gm.w));
-                x = lds4(sA, o);
-                put4(sA, o, make_float4(x.x * gp.x, x.y * gp.y, x.z * gp.z, x.w * gp.w));
-                x = lds4(sB, o);
-                put4(sB, o, make_float4(x.x * inv.x, x.y * inv.y, x.z * inv.z, x.w * inv.w));
+                put4(sR, o, make_float4(xr[m].x * gq.x, xr[m].y * gq.y, xr[m].z * gq.z, xr[m].w * gq.w));
+                put4(sA, o, make_float4(xa[m].x * gv.x, xa[m].y * gv.y, xa[m].z * gv.z, xa[m].w * gv.w));
+                put4(sB, o, make_float4(xb[m].x * inv.x, xb[m].y * inv.y, xb[m].z * inv.z, xb[m].w * inv.w));
             }
         } else {
         // ---- inputs of the chunk into LDS (the last chunk is there already)
@@ -777,13 +788,12 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                     });
             };
 
-            // ---- pass 1: Grams dy v^T, dsa v^T; dk bracket; kt terms of dr, da
+            // ---- pass 1: Grams dy v^T, dsa v^T; dk bracket; kt terms of dr, da.
+            // v is not read after the Grams: sa replaces it during the pass.
             gram(sDY, sD, sVS, none);
             __syncthreads();
             refresh();
             value_terms(XK, sK);
-            __syncthreads();
-            refresh();
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
@@ -910,6 +920,10 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                             n += 2;
                         }
                 });
+            // the next chunk's copies land before the barrier that publishes
+            // them; the wait (for every earlier memory operation of the wave)
+            // comes before dv's stores, so that it does not wait for them
+            if (kDma && c > 0) wait_dma();
 #pragma unroll
             for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
@@ -917,8 +931,6 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                     const int t = 16 * TB[lt] + 4 * g + i;
                     bstore(odv, ooff(t), XV[lt][i]);
                 }
-            // the next chunk's copies land before the barrier that publishes them
-            if (kDma && c > 0) wait_dma();
             __syncthreads();
             refresh();
         };
