@@ -15,6 +15,11 @@ peak (157.3 TFLOP/s, the same for dense fp32 MFMA and packed fp32 VALU).
 `fwd_only_tokens_per_s` times the forward alone without checkpoints
 (inference).  `cpu_baseline` times the fp64 oracle on a bounded sample of
 whole (b, h) recurrences of the same workload on the host's cores.
+
+A workload with T = 1 (``--workload decode_b256_t1_h32_n64``) times the
+decode step of batched inference instead: one forward step of every (b, h)
+from its carry-in state, bound by HBM bandwidth (each (b, h) reads and
+writes its N x N fp32 state).
 """
 import argparse
 import json
@@ -47,6 +52,100 @@ def algorithmic(wl):
     return fwd_flops, bwd_flops, fwd_bytes, bwd_bytes
 
 
+DECODE_METRIC = "WKV7 decode step tokens/sec at 1 GPU; % of HBM roofline (rocprof)"
+
+
+def decode_bytes(wl):
+    """Algorithmic HBM bytes of one decode step: the state in and out, six
+    input vectors in, y out."""
+    eb = 4 if wl.dtype == "f32" else 2
+    N = wl.N
+    return wl.B * wl.H * (2 * 4 * N * N + 6 * eb * N + 4 * N)
+
+
+def decode_bench(args, wl):
+    import torch
+
+    import oracle
+    from linear_attention_rnn_wkv7_amd import api
+    from linear_attention_rnn_wkv7_amd.synthetic import make_inputs
+
+    names = ("r", "w", "k", "v", "a", "b")
+    inp = make_inputs(wl, device="cuda")
+    B, H, N = wl.B, wl.H, wl.N
+    y = torch.empty((B, 1, H, N), device="cuda", dtype=torch.float32)
+    sT = torch.empty((B, H, N, N), device="cuda", dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        api.wkv7_forward(*(inp[n] for n in names), inp["s0"], out=(y, sT, None), stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    for n, x in (("y", y), ("sT", sT)):
+        if not torch.isfinite(x).all():
+            raise RuntimeError(f"non-finite values in {n}")
+    nbytes = decode_bytes(wl)
+    achieved = nbytes / (ms * 1e-3)
+    rec = {
+        "metric": DECODE_METRIC,
+        "value": B / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": 1, "H": H, "N": N,
+                   "input_dtype": wl.dtype, "s0": wl.has_s0},
+        "roofline": {
+            "kernel": "wkv7_decode_kernel",
+            "bound": "hbm",
+            "achieved": achieved / 1e9,
+            "peak": PEAK_HBM / 1e9,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM,
+            "traffic": measured_traffic("wkv7_decode_kernel", wl.name),
+        },
+    }
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, device="cuda", dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_bytes"] = args.copy_bytes
+    if not args.no_cpu_baseline:
+        host = {n: inp[n].cpu().double().numpy() for n in names}
+        s0 = inp["s0"].cpu().double().numpy()
+        cores = oracle.default_threads()
+        reps, t0 = 0, time.perf_counter()
+        while True:   # whole decode steps of every (b, h), up to the budget
+            oracle.forward(*(host[n] for n in names), s0=s0, threads=cores)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_budget:
+                break
+        rec["cpu_baseline"] = {"value": reps * B / el, "unit": "tokens/s", "cores": cores,
+                               "kind": "oracle",
+                               "sample": f"{reps} whole decode steps of all {B * H} (b,h), fp64, "
+                                         f"in {el:.2f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs,
     or None when absent or taken on a different kernel source."""
@@ -57,7 +156,7 @@ def measured_traffic(kernel, workload):
         rec = json.load(f)
     from linear_attention_rnn_wkv7_amd.profiling import kernel_sha
 
-    if rec.get("kernel_sha") != kernel_sha():
+    if rec.get("kernel_sha") != kernel_sha(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -135,6 +234,8 @@ def main():
     from linear_attention_rnn_wkv7_amd.synthetic import WORKLOADS, make_inputs
 
     wl = WORKLOADS[args.workload]
+    if wl.T == 1:
+        return decode_bench(args, wl)
     names = ("r", "w", "k", "v", "a", "b")
     inp = make_inputs(wl, device="cuda")
     B, T, H, N, C = wl.B, wl.T, wl.H, wl.N, wl.chunk

@@ -121,7 +121,10 @@ size_t wkv7_backward_workspace_bytes(const wkv7_shape *shape, int ckpt_provided)
  *   sT   : final state, fp32 [B][H][N][N]; NULL skips it.
  *   ckpt : checkpoint record for wkv7_backward, wkv7_checkpoint_bytes(shape)
  *          bytes (states every C steps and the per-step sa); NULL skips it.
- * With T == 0, sT receives s0 (or zeros). */
+ * With T == 0, sT receives s0 (or zeros).  T == 1 (one decode step of
+ * batched inference from a carry-in state) runs a single-step kernel that
+ * streams each (b, h)'s state through once; there sT may be s0 itself (the
+ * state is updated in place).  Otherwise no output may overlap an input. */
 int wkv7_forward(const wkv7_shape *shape,
                  const void *r, const void *w, const void *k, const void *v,
                  const void *a, const void *b, const float *s0,

@@ -16,9 +16,10 @@
 // Hb = H diag(g_63), the gradient of the state after step t is
 //   G_t = (Hb + sum_{u>=t} dy_u rb_u^T + sum_{u>t} dsa_u ab_u^T) diag(1/g_t),
 // and dsa_t = G_t b_t.  dsa is the only quantity with a serial dependency:
-// phase 1 runs it step by step (VALU, the state G scaled by g so that the
-// decay costs nothing per element).  Phase 2 then forms every gradient with
-// dense contractions (MFMA), e.g.
+//   dsa_t = Hb bt_t + sum_{u>=t} dy_u (rb_u.bt_t) + sum_{u>t} dsa_u (ab_u.bt_t),
+// a unit-triangular system over the chunk's steps, solved in 16-step blocks
+// (the inverse of each diagonal block formed step by step on the VALU, the
+// rest on MFMA).  Every gradient is then a dense contraction (MFMA), e.g.
 //   dk_t = (1/g_t) (Hb^T v_t + sum_{u>=t} rb_u (dy_u.v_t) + sum_{u>t} ab_u (dsa_u.v_t))
 //   dr_t = g_t (S0^T dy_t + sum_{u<=t} kt_u (v_u.dy_t) + bt_u (sa_u.dy_t))
 // and dw from the per-column identity

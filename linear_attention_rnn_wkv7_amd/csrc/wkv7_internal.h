@@ -47,6 +47,8 @@ inline bool chunk_offsets_fit(int64_t T, int64_t H)
 size_t sub_bytes(int64_t B, int64_t H, int64_t N, int chunk);
 
 hipError_t launch_forward(const FwdLaunch &a, hipStream_t stream);
+// The single-step forward (T = 1) of wkv7_decode.hip.
+hipError_t launch_decode(const FwdLaunch &a, hipStream_t stream);
 // The forward for N = 64 on a scan plus matrix-core helper waves
 // (wkv7_fwdc.hip); it needs checkpoints on 32-step block starts.
 bool forward_chunked_supported(const FwdLaunch &a);

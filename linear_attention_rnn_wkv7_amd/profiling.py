@@ -20,16 +20,25 @@ import re
 import statistics
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCES = ("linear_attention_rnn_wkv7_amd/csrc/wkv7_bwd.hip",
-                  "linear_attention_rnn_wkv7_amd/csrc/wkv7_bwdc.hip",
-                  "linear_attention_rnn_wkv7_amd/csrc/wkv7_fwd.hip",
-                  "linear_attention_rnn_wkv7_amd/csrc/wkv7_fwdc.hip",
-                  "linear_attention_rnn_wkv7_amd/csrc/wkv7_device.h")
+_CSRC = "linear_attention_rnn_wkv7_amd/csrc/"
+KERNEL_SOURCES = tuple(_CSRC + f for f in ("wkv7_bwd.hip", "wkv7_bwdc.hip", "wkv7_fwd.hip",
+                                           "wkv7_fwdc.hip", "wkv7_decode.hip", "wkv7_device.h"))
+# the sources each kernel is built from (its traffic record is stale once
+# one of them changes)
+_KERNEL_FILES = {
+    "wkv7_bwdc_kernel": ("wkv7_bwdc.hip", "wkv7_device.h"),
+    "wkv7_fwdc_kernel": ("wkv7_fwdc.hip", "wkv7_device.h"),
+    "wkv7_bwd_kernel": ("wkv7_bwd.hip", "wkv7_device.h"),
+    "wkv7_fwd_kernel": ("wkv7_fwd.hip", "wkv7_device.h"),
+    "wkv7_decode_kernel": ("wkv7_decode.hip", "wkv7_device.h"),
+}
 
 
-def kernel_sha(sources=KERNEL_SOURCES):
+def kernel_sha(kernel=None):
+    """Hash of the sources of `kernel` (all kernel sources when None)."""
+    files = KERNEL_SOURCES if kernel is None else tuple(_CSRC + f for f in _KERNEL_FILES[kernel])
     h = hashlib.sha256()
-    for rel in sources:
+    for rel in files:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -120,7 +129,7 @@ def traffic(fetch_csv, write_csv, kernel, copy_bytes, workload, cmd, out):
     rec = {
         "workload": workload,
         "kernel": kernel,
-        "kernel_sha": kernel_sha(),
+        "kernel_sha": kernel_sha(kernel),
         "command": cmd,
         "fetch_kib_per_dispatch": f_k,
         "write_kib_per_dispatch": w_k,

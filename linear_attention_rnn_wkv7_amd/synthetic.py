@@ -52,6 +52,9 @@ WORKLOADS = {
         Workload("b8_t4096_h32_n64", 8, 4096, 32, 64, "f32", False, False, 1003),
         Workload("b16_t4096_h64_n64_bf16", 16, 4096, 64, 64, "bf16", True, False, 1004),
         Workload("long_b1_t65536_h32_n64", 1, 65536, 32, 64, "f32", True, True, 1005),
+        # one decode step of batched inference: 256 sequences of a width-2048
+        # model (32 heads of 64), each with its carry-in state
+        Workload("decode_b256_t1_h32_n64", 256, 1, 32, 64, "f32", True, False, 1006),
     )
 }
 WORKLOAD_ORDER = list(WORKLOADS)
