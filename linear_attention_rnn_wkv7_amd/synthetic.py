@@ -65,8 +65,12 @@ def custom(B, T, H, N, dtype="f32", has_s0=True, has_dsT=True, seed=7, chunk=64)
                     has_s0, has_dsT, seed, chunk)
 
 
-def make_inputs(wl: Workload, device="cpu", seed: Optional[int] = None):
-    """Return a dict of tensors r, w, k, v, a, b, dy, s0 (or None), dsT (or None)."""
+def make_inputs(wl: Workload, device="cpu", seed: Optional[int] = None, fused=False):
+    """Return a dict of tensors r, w, k, v, a, b, dy, s0 (or None), dsT (or None).
+
+    fused=True returns the same draws before w, a and b are formed, in their
+    places: w holds the decay pre-activation x, a the normalised key kk and
+    b the gate sigmoid(z) (the inputs of the fused form of the library)."""
     dev = torch.device(device)
     g = torch.Generator(device=dev)
     g.manual_seed(wl.seed if seed is None else seed)
@@ -79,12 +83,17 @@ def make_inputs(wl: Workload, device="cpu", seed: Optional[int] = None):
     r = randn(shp)
     k = randn(shp)
     v = randn(shp)
-    w = torch.exp(-DECAY_COEFF * torch.sigmoid(randn(shp)))
+    x = randn(shp)
     kk = randn(shp)
     kk = kk / (torch.linalg.vector_norm(kk, dim=-1, keepdim=True) + 1e-12)
-    a = -kk
-    b = kk * torch.sigmoid(randn(shp))
-    del kk
+    gate = torch.sigmoid(randn(shp))
+    if fused:
+        w, a, b = x, kk, gate
+    else:
+        w = torch.exp(-DECAY_COEFF * torch.sigmoid(x))
+        a = -kk
+        b = kk * gate
+    del x, kk, gate
     dy = randn(shp)
     s0 = 0.1 * randn((wl.B, wl.H, wl.N, wl.N)) if wl.has_s0 else None
     dsT = randn((wl.B, wl.H, wl.N, wl.N)) if wl.has_dsT else None

@@ -306,6 +306,75 @@ def pin_exact_rational(rng, lib=None, T=3, N=2):
     return max(errs)
 
 
+# --------------------------------------- fused time-mix inputs (oracle.fused)
+def rand_fused(rng, B, T, H, N):
+    """omega ~ N(0,1), kk unit per (b,t,h), ag = sigmoid(N(0,1)), in the
+    recurrence's positional slots of w, a, b."""
+    shp = (B, T, H, N)
+    d = {n: rng.standard_normal(shp) for n in ("r", "k", "v", "dy")}
+    d["w"] = rng.standard_normal(shp)
+    kk = rng.standard_normal(shp)
+    d["a"] = kk / np.linalg.norm(kk, axis=-1, keepdims=True)
+    d["b"] = 1.0 / (1.0 + np.exp(-rng.standard_normal(shp)))
+    d["s0"] = 0.3 * rng.standard_normal((B, H, N, N))
+    d["dsT"] = rng.standard_normal((B, H, N, N))
+    return d
+
+
+def _fused_loss(d, lib=None):
+    import oracle.fused as F
+    y, sT = F.forward(*(d[n] for n in NAMES_IN), s0=d["s0"], lib=lib)
+    return float(np.sum(d["dy"] * y)) + float(np.sum(d["dsT"] * sT))
+
+
+def pin_fused_finite_differences(rng, lib=None, B=1, T=4, H=2, N=3, h=1e-6):
+    """Central differences of the loss through the formed inputs, for every
+    element of r, omega, k, v, kk, ag and s0."""
+    import oracle.fused as F
+    d = rand_fused(rng, B, T, H, N)
+    g = F.backward(*(d[n] for n in NAMES_IN), d["dy"], s0=d["s0"], dsT=d["dsT"], lib=lib)
+    worst = 0.0
+    for n, gn in list(zip(NAMES_IN, NAMES_GRAD)) + [("s0", "ds0")]:
+        fd = np.zeros_like(d[n])
+        for idx in np.ndindex(d[n].shape):
+            keep = d[n][idx]
+            d[n][idx] = keep + h
+            lp = _fused_loss(d, lib)
+            d[n][idx] = keep - h
+            lm = _fused_loss(d, lib)
+            d[n][idx] = keep
+            fd[idx] = (lp - lm) / (2 * h)
+        worst = max(worst, rel(g[gn], fd))
+    return worst
+
+
+def pin_fused_torch_autograd(rng, lib=None, B=1, T=5, H=2, N=4):
+    """torch autograd of a plain loop that forms w, a, b from omega, kk, ag."""
+    import torch
+
+    import oracle.fused as F
+    d = rand_fused(rng, B, T, H, N)
+    g = F.backward(*(d[n] for n in NAMES_IN), d["dy"], s0=d["s0"], dsT=d["dsT"], lib=lib)
+    tv = {n: torch.tensor(d[n], dtype=torch.float64, requires_grad=True)
+          for n in NAMES_IN + ("s0",)}
+    c = float(np.exp(-0.5))
+    L = torch.zeros((), dtype=torch.float64)
+    for bb in range(B):
+        for h in range(H):
+            S = tv["s0"][bb, h]
+            for t in range(T):
+                om, kk, ag = tv["w"][bb, t, h], tv["a"][bb, t, h], tv["b"][bb, t, h]
+                w = torch.exp(-c * torch.sigmoid(om))
+                a, b = -kk, kk * ag
+                k, v, r = tv["k"][bb, t, h], tv["v"][bb, t, h], tv["r"][bb, t, h]
+                S = S * w[None, :] + torch.outer(v, k) + torch.outer(S @ a, b)
+                L = L + torch.dot(torch.tensor(d["dy"][bb, t, h]), S @ r)
+            L = L + (torch.tensor(d["dsT"][bb, h]) * S).sum()
+    L.backward()
+    return max(rel(g[gn], tv[n].grad.numpy())
+               for n, gn in list(zip(NAMES_IN, NAMES_GRAD)) + [("s0", "ds0")])
+
+
 ALL_PINS = {
     "golden_n1": (lambda rng, lib: pin_golden("hand_n1_t2.txt", lib), 1e-15),
     "golden_n2": (lambda rng, lib: pin_golden("hand_n2_t1.txt", lib), 1e-15),
@@ -318,4 +387,6 @@ ALL_PINS = {
     "identities": (pin_identities, 1e-11),
     "torch_autograd": (pin_torch_autograd, 1e-12),
     "exact_rational": (pin_exact_rational, 1e-13),
+    "fused_finite_differences": (pin_fused_finite_differences, 1e-7),
+    "fused_torch_autograd": (pin_fused_torch_autograd, 1e-12),
 }
