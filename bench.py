@@ -16,6 +16,12 @@ peak (157.3 TFLOP/s, the same for dense fp32 MFMA and packed fp32 VALU).
 (inference).  `cpu_baseline` times the fp64 oracle on a bounded sample of
 whole (b, h) recurrences of the same workload on the host's cores.
 
+``--fused`` runs the same step on the fused time-mix inputs (omega, kk and
+the gate in the places of w, a, b; the library forms w, a, b and returns
+d omega, d kk, d gate) and adds ``unfused_pipeline_ms``: the same result
+from the plain kernels with torch forming w, a, b before and chaining the
+gradients after, the element-wise HBM passes the fused form saves.
+
 A workload with T = 1 (``--workload decode_b256_t1_h32_n64``) times the
 decode step of batched inference instead: one forward step of every (b, h)
 from its carry-in state, bound by HBM bandwidth (each (b, h) reads and
@@ -146,6 +152,41 @@ def decode_bench(args, wl):
     print(json.dumps(rec), flush=True)
 
 
+def unfused_pipeline_ms(api, inp, names, C, ck, ws, y, sT, grads, stream, args):
+    """The fused step's result without fusion: torch forms w, a, b from
+    omega, kk and the gate, the plain kernels run, torch chains dw, da, db
+    into d omega, d kk, d gate.  Mean ms per step over the same step count."""
+    import math
+
+    import torch
+
+    c = math.exp(-0.5)
+    om, kk, ag = inp["w"], inp["a"], inp["b"]
+
+    def step():
+        sg = torch.sigmoid(om)
+        w = torch.exp(-c * sg)
+        a = -kk
+        b = kk * ag
+        plain = (inp["r"], w, inp["k"], inp["v"], a, b)
+        api.wkv7_forward(*plain, inp["s0"], chunk=C, want_ckpt=True, out=(y, sT, ck),
+                         stream=stream)
+        g = api.wkv7_backward(*plain, inp["dy"], inp["s0"], inp["dsT"], ck, chunk=C, workspace=ws,
+                              out=grads, stream=stream)
+        return (g["dw"] * w * (-c) * sg * (1 - sg), -g["da"] + ag * g["db"], kk * g["db"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / args.steps
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs,
     or None when absent or taken on a different kernel source."""
@@ -161,11 +202,13 @@ def measured_traffic(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, wl, budget_s):
-    """Time the fp64 oracle (fwd + bwd) on whole (b, h) recurrences."""
+def cpu_baseline(inp, wl, budget_s, fused=False):
+    """Time the fp64 oracle (fwd + bwd) on whole (b, h) recurrences (its
+    fused-input form with fused=True)."""
     import numpy as np
 
     import oracle
+    import oracle.fused
     from linear_attention_rnn_wkv7_amd.synthetic import state_slice, vec_slice
 
     cores = oracle.default_threads()
@@ -186,9 +229,9 @@ def cpu_baseline(inp, wl, budget_s):
         sl, s0, dsT = sample(pairs)
         threads = min(cores, len(pairs))
         t = time.perf_counter()
-        oracle.forward(*(sl[n] for n in names[:6]), s0=s0, want_sT=True, threads=threads)
-        oracle.backward(*(sl[n] for n in names[:6]), sl["dy"], s0=s0, dsT=dsT,
-                        threads=threads)
+        orc = oracle.fused if fused else oracle
+        orc.forward(*(sl[n] for n in names[:6]), s0=s0, want_sT=True, threads=threads)
+        orc.backward(*(sl[n] for n in names[:6]), sl["dy"], s0=s0, dsT=dsT, threads=threads)
         return time.perf_counter() - t, threads
 
     all_pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)]
@@ -217,6 +260,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused", action="store_true",
+                    help="fused time-mix inputs (WKV7_FUSED_INPUTS)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run a plain device copy of this many bytes (the "
                          "reference point for the HBM traffic counters)")
@@ -237,7 +282,8 @@ def main():
     if wl.T == 1:
         return decode_bench(args, wl)
     names = ("r", "w", "k", "v", "a", "b")
-    inp = make_inputs(wl, device="cuda")
+    fused = args.fused
+    inp = make_inputs(wl, device="cuda", fused=fused)
     B, T, H, N, C = wl.B, wl.T, wl.H, wl.N, wl.chunk
     dev = inp["r"].device
     f32 = torch.float32
@@ -256,11 +302,11 @@ def main():
         if ev:
             ev[0].record(stream)
         api.wkv7_forward(*(inp[n] for n in names), inp["s0"], chunk=C, want_ckpt=True,
-                         out=(y, sT, ck), stream=stream)
+                         out=(y, sT, ck), stream=stream, fused=fused)
         if ev:
             ev[1].record(stream)
         api.wkv7_backward(*(inp[n] for n in names), inp["dy"], inp["s0"], inp["dsT"], ck,
-                          chunk=C, workspace=ws, out=grads, stream=stream)
+                          chunk=C, workspace=ws, out=grads, stream=stream, fused=fused)
         if ev:
             ev[2].record(stream)
 
@@ -283,7 +329,7 @@ def main():
     f0.record(stream)
     for _ in range(args.steps):
         api.wkv7_forward(*(inp[n] for n in names), inp["s0"], chunk=C, want_ckpt=False,
-                         out=(y, sT, None), stream=stream)
+                         out=(y, sT, None), stream=stream, fused=fused)
     f1.record(stream)
     torch.cuda.synchronize()
     fwd_only_ms = f0.elapsed_time(f1) / args.steps
@@ -314,7 +360,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "N": N, "chunk": C,
-                   "input_dtype": wl.dtype, "s0": wl.has_s0, "dsT": wl.has_dsT},
+                   "input_dtype": wl.dtype, "s0": wl.has_s0, "dsT": wl.has_dsT,
+                   **({"fused_inputs": True} if fused else {})},
         "roofline": {
             "kernel": kernel,
             "bound": "mfma" if chunked else "alu",
@@ -329,6 +376,9 @@ def main():
         "fwd_only_tokens_per_s": tokens / (fwd_only_ms * 1e-3),
         "fwd_bwd_roofline_frac": t_roof / (ms * 1e-3),
     }
+    if fused:
+        rec["unfused_pipeline_ms"] = unfused_pipeline_ms(api, inp, names, C, ck, ws, y, sT,
+                                                         grads, stream, args)
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes, device=dev, dtype=torch.uint8)
         dst = torch.empty_like(src)
@@ -337,7 +387,7 @@ def main():
         torch.cuda.synchronize()
         rec["copy_bytes"] = args.copy_bytes
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget, fused=fused)
     print(json.dumps(rec), flush=True)
 
 

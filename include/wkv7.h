@@ -81,6 +81,23 @@ typedef enum {
     WKV7_ALGO_CHUNKED = 2
 } wkv7_algo;
 
+/* Bits of wkv7_shape.flags.
+ *   WKV7_FUSED_INPUTS : the w, a, b arguments carry the time-mix values the
+ *     Foundry rx_pretrain.c page forms them from in tm_pre_forward, and the
+ *     library forms them itself: w holds the decay pre-activation omega
+ *     (w = exp(-c * sigmoid(omega)), c = RX_WDECAY_COEFF = exp(-0.5)), a the
+ *     normalised key kk (a = -kk) and b the gate ag (b = kk * ag).  The
+ *     backward then returns d omega, d kk and d ag (the page's time-mix
+ *     backward: dw * w * (-c) * sigmoid * (1 - sigmoid), -da + ag * db,
+ *     kk * db) in the places of dw, da and db, saving the element-wise
+ *     passes over those tensors before and after the scan.  Needs N = 64,
+ *     C = 64 and, for T > 1, T*H*64*4 < 2^31 bytes, with algo AUTO or
+ *     CHUNKED (WKV7_ERR_UNSUPPORTED otherwise); the checkpoint record of a
+ *     fused forward is for a fused backward. */
+enum {
+    WKV7_FUSED_INPUTS = 1
+};
+
 typedef struct {
     int64_t B;      /* batch, >= 0 */
     int64_t T;      /* time steps, >= 0 */
@@ -90,7 +107,7 @@ typedef struct {
     int32_t chunk;  /* checkpoint interval C: 0 means 64; else a multiple of
                        8 in [8, 4096] */
     int32_t algo;   /* wkv7_algo (backward only) */
-    int32_t reserved; /* must be 0 */
+    int32_t flags;  /* 0 or WKV7_FUSED_INPUTS; other bits must be 0 */
 } wkv7_shape;
 
 enum {

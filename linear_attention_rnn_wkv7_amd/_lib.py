@@ -18,10 +18,13 @@ EXPORTS = ("wkv7_checkpoint_bytes", "wkv7_backward_workspace_bytes", "wkv7_forwa
            "wkv7_backward", "wkv7_status_string", "wkv7_abi_version")
 
 
+WKV7_FUSED_INPUTS = 1   # wkv7_shape.flags bit
+
+
 class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("N", ctypes.c_int64), ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32),
-                ("algo", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("algo", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class Wkv7Error(RuntimeError):

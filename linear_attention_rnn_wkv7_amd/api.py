@@ -26,8 +26,9 @@ _ALGOS = {"auto": _lib.WKV7_ALGO_AUTO, "scan": _lib.WKV7_ALGO_SCAN,
           "chunked": _lib.WKV7_ALGO_CHUNKED}
 
 
-def make_shape(B, T, H, N, dtype=torch.float32, chunk=64, algo="auto"):
-    return _lib.Shape(B, T, H, N, _VEC_DTYPES[dtype], chunk, _ALGOS[algo], 0)
+def make_shape(B, T, H, N, dtype=torch.float32, chunk=64, algo="auto", fused=False):
+    return _lib.Shape(B, T, H, N, _VEC_DTYPES[dtype], chunk, _ALGOS[algo],
+                      _lib.WKV7_FUSED_INPUTS if fused else 0)
 
 
 def _check_vecs(names, tensors):
@@ -63,8 +64,11 @@ def wkv7_backward_workspace_bytes(B, T, H, N, dtype=torch.float32, chunk=64, ckp
 
 
 def wkv7_forward(r, w, k, v, a, b, s0=None, *, chunk=64, want_y=True, want_sT=True,
-                 want_ckpt=False, stream=None, out=None):
+                 want_ckpt=False, stream=None, out=None, fused=False):
     """Run the forward scan.  Returns (y, sT, ckpt); unwanted outputs are None.
+
+    fused=True (WKV7_FUSED_INPUTS): w, a, b carry omega, kk and the gate, and
+    the library forms w = exp(-exp(-0.5) sigmoid(omega)), a = -kk, b = kk gate.
 
     ckpt is the flat fp32 checkpoint record (states every `chunk` steps, then
     the per-step sa) that wkv7_backward consumes.
@@ -82,7 +86,7 @@ def wkv7_forward(r, w, k, v, a, b, s0=None, *, chunk=64, want_y=True, want_sT=Tr
     if want_ckpt and ckpt is None:
         ckpt = torch.empty(wkv7_checkpoint_bytes(B, T, H, N, dt, chunk) // 4, device=dev,
                            dtype=torch.float32)
-    sh = make_shape(B, T, H, N, dt, chunk)
+    sh = make_shape(B, T, H, N, dt, chunk, fused=fused)
     rc = _lib.lib().wkv7_forward(ctypes.byref(sh), *map(_ptr, (r, w, k, v, a, b, s0)),
                                  _ptr(y if want_y else None), _ptr(sT if want_sT else None),
                                  _ptr(ckpt if want_ckpt else None), _stream(stream))
@@ -91,10 +95,13 @@ def wkv7_forward(r, w, k, v, a, b, s0=None, *, chunk=64, want_y=True, want_sT=Tr
 
 
 def wkv7_backward(r, w, k, v, a, b, dy, s0=None, dsT=None, ckpt=None, *, chunk=64,
-                  want_ds0=True, workspace=None, stream=None, out=None, algo="auto"):
+                  want_ds0=True, workspace=None, stream=None, out=None, algo="auto",
+                  fused=False):
     """Run the reverse scan.  Returns dict(dr, dw, dk, dv, da, db, ds0).
 
-    algo: "auto", "scan" or "chunked" (wkv7_algo)."""
+    algo: "auto", "scan" or "chunked" (wkv7_algo).  fused=True: the inputs
+    as for wkv7_forward(fused=True), and dw, da, db hold d omega, d kk and
+    d gate."""
     (B, T, H, N), dt = _check_vecs("rwkvab dy", (r, w, k, v, a, b, dy))
     _check_state("s0", s0, B, H, N)
     _check_state("dsT", dsT, B, H, N)
@@ -112,7 +119,7 @@ def wkv7_backward(r, w, k, v, a, b, dy, s0=None, dsT=None, ckpt=None, *, chunk=6
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    sh = make_shape(B, T, H, N, dt, chunk, algo)
+    sh = make_shape(B, T, H, N, dt, chunk, algo, fused=fused)
     rc = _lib.lib().wkv7_backward(
         ctypes.byref(sh), *map(_ptr, (r, w, k, v, a, b, s0, dy, dsT, ckpt)),
         *map(_ptr, (grads[n] for n in names)), _ptr(grads["ds0"]),

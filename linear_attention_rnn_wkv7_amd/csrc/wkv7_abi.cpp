@@ -13,7 +13,7 @@ constexpr size_t kAlign = 256;   // workspace sub-buffer alignment
 
 struct Dims {
     int64_t B, T, H, N, C, nck;
-    int dtype, algo;
+    int dtype, algo, fused;
     size_t vec_elems, state_elems;   // per tensor
 };
 
@@ -27,7 +27,7 @@ int check_shape(const wkv7_shape *s, Dims *d)
     if (!s) return WKV7_ERR_INVALID;
     if (s->B < 0 || s->T < 0 || s->H < 0 || s->N <= 0) return WKV7_ERR_INVALID;
     if (s->dtype != WKV7_F32 && s->dtype != WKV7_BF16) return WKV7_ERR_INVALID;
-    if (s->algo < WKV7_ALGO_AUTO || s->algo > WKV7_ALGO_CHUNKED || s->reserved != 0)
+    if (s->algo < WKV7_ALGO_AUTO || s->algo > WKV7_ALGO_CHUNKED || (s->flags & ~WKV7_FUSED_INPUTS) != 0)
         return WKV7_ERR_INVALID;
     const int64_t C = s->chunk == 0 ? 64 : s->chunk;
     if (C < 8 || C > 4096 || C % 8 != 0) return WKV7_ERR_INVALID;
@@ -48,9 +48,18 @@ int check_shape(const wkv7_shape *s, Dims *d)
     d->nck = nck;
     d->dtype = s->dtype;
     d->algo = s->algo;
+    d->fused = (s->flags & WKV7_FUSED_INPUTS) != 0;
     d->vec_elems = (size_t)vec;
     d->state_elems = (size_t)st;
     return WKV7_OK;
+}
+
+// Fused inputs run in the chunk forms (and the single-step kernel): N = 64,
+// C = 64, 32-bit offsets within a batch row; not with the step scan.
+bool fused_supported(const Dims &d)
+{
+    return d.N == 64 && d.C == 64 && d.algo != WKV7_ALGO_SCAN &&
+           (d.T <= 1 || wkv7::chunk_offsets_fit(d.T, d.H));
 }
 
 bool aligned(const void *p)
@@ -138,6 +147,7 @@ int wkv7_forward(const wkv7_shape *shape, const void *r, const void *w, const vo
     }
     for (const void *p : {(const void *)s0, (const void *)y, (const void *)sT, (const void *)ckpt})
         if (!aligned(p)) return WKV7_ERR_INVALID;
+    if (d.fused && !fused_supported(d)) return WKV7_ERR_UNSUPPORTED;
 
     if (d.T == 0) {
         if (!sT) return WKV7_OK;
@@ -156,6 +166,7 @@ int wkv7_forward(const wkv7_shape *shape, const void *r, const void *w, const vo
     L.N = d.N;
     L.dtype = d.dtype;
     L.chunk = (int)d.C;
+    L.fused = d.fused;
     return hip_status(wkv7::launch_forward(L, stream));
 }
 
@@ -187,6 +198,7 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
     if (d.algo == WKV7_ALGO_CHUNKED &&
         !(d.N == 64 && d.C == 64 && (d.T == 0 || wkv7::chunk_offsets_fit(d.T, d.H))))
         return WKV7_ERR_UNSUPPORTED;
+    if (d.fused && !fused_supported(d)) return WKV7_ERR_UNSUPPORTED;
     if (d.T == 0) {
         if (!ds0) return WKV7_OK;
         return hip_status(wkv7::launch_fill(ds0, dsT, d.state_elems, stream));
@@ -213,6 +225,7 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
         F.N = d.N;
         F.dtype = d.dtype;
         F.chunk = (int)d.C;
+        F.fused = d.fused;
         rc = hip_status(wkv7::launch_forward(F, stream));
         if (rc != WKV7_OK) return rc;
         ck = own;
@@ -233,6 +246,7 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
     L.dtype = d.dtype;
     L.chunk = (int)d.C;
     L.algo = d.algo;
+    L.fused = d.fused;
     return hip_status(wkv7::launch_backward(L, stream));
 }
 
@@ -250,7 +264,7 @@ const char *wkv7_status_string(int status)
 
 int wkv7_abi_version(void)
 {
-    return 102;
+    return 103;
 }
 
 }  // extern "C"

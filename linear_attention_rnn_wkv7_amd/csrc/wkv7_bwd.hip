@@ -501,6 +501,12 @@ size_t sub_bytes(int64_t B, int64_t H, int64_t N, int chunk)
 hipError_t launch_backward(const BwdLaunch &a, hipStream_t stream)
 {
     const int *only = nullptr;
+    if (a.fused) {
+        // the decays formed from fused inputs lie in [exp(-exp(-0.5)), 1]: the
+        // chunk form takes every head (the caller checked that it applies)
+        if (!chunked_backward_supported(a)) return hipErrorInvalidValue;
+        return launch_backward_chunked(a, a.flags, stream);
+    }
     if (a.algo != 1 && chunked_backward_supported(a)) {
         const hipError_t e = launch_backward_chunked(a, a.flags, stream);
         if (e != hipSuccess) return e;

@@ -29,6 +29,14 @@
 // chain rule (the gradient-state inner product per column is conserved up to
 // the terms each step adds).
 //
+// With fused inputs the w, a, b slots hold the decay pre-activation omega,
+// the normalised key kk and the gate ag of the page's tm_pre_forward: the
+// kernel forms w = exp(-c sigmoid(omega)) where it takes the decay's
+// cumulative product, a = -kk and b = kk ag in the rescaling pass, and
+// returns d omega = w dw (-c) s (1 - s) (s = sigmoid(omega) = -ln(w) / c),
+// d kk = -da + ag db and d ag = kk db in the places of dw, da, db (the
+// page's time-mix backward).  Those decays always lie in [exp(-c), 1].
+//
 // The rescaled form needs the cumulative decay to stay well inside fp32
 // range and w not too small (dw divides by w).  A chunk whose decays fall
 // outside [kWMin, 1] or whose cumulative decay drops below kGMin marks its
@@ -213,7 +221,7 @@ __device__ __forceinline__ float bcast_group(float x)
     return __builtin_bit_cast(float, (G0 & 2) ? q[1] : q[0]);
 }
 
-template <typename TIn>
+template <typename TIn, bool kFused>
 __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 {
     // chunk vectors, [step][feature] swizzled: cumulative decay, rb, ab, kt,
@@ -302,7 +310,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
-            const float d = q == 1 ? 1.f : 0.f;
+            const float d = q == 1 ? (kFused ? -INFINITY : 1.f) : 0.f;
             put4(dst_[q], sw(t, j4), t < Lcc ? InQuad<TIn>::f32(pre[q][m]) : make_float4(d, d, d, d));
         }
     };
@@ -340,6 +348,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         float pr = 1.f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
+            if constexpr (kFused) gn[u] = decay_from_pre(gn[u]);
             if (8 * seg + u >= Lcc) gn[u] = 1.f;   // past the end of the sequence
             pr *= gn[u];
         }
@@ -426,8 +435,15 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                 const float4 kx = t < Lc ? InQuad<TIn>::f32(pre[2][m]) : make_float4(0.f, 0.f, 0.f, 0.f);
                 put4(sK, o, make_float4(kx.x * inv.x, kx.y * inv.y, kx.z * inv.z, kx.w * inv.w));
                 put4(sR, o, make_float4(xr[m].x * gq.x, xr[m].y * gq.y, xr[m].z * gq.z, xr[m].w * gq.w));
-                put4(sA, o, make_float4(xa[m].x * gv.x, xa[m].y * gv.y, xa[m].z * gv.z, xa[m].w * gv.w));
-                put4(sB, o, make_float4(xb[m].x * inv.x, xb[m].y * inv.y, xb[m].z * inv.z, xb[m].w * inv.w));
+                if constexpr (kFused) {   // xa: kk, xb: gate; a = -kk, b = kk gate
+                    const float4 ka = xa[m], gb = xb[m];
+                    put4(sA, o, make_float4(-ka.x * gv.x, -ka.y * gv.y, -ka.z * gv.z, -ka.w * gv.w));
+                    put4(sB, o, make_float4(ka.x * gb.x * inv.x, ka.y * gb.y * inv.y, ka.z * gb.z * inv.z,
+                                            ka.w * gb.w * inv.w));
+                } else {
+                    put4(sA, o, make_float4(xa[m].x * gv.x, xa[m].y * gv.y, xa[m].z * gv.z, xa[m].w * gv.w));
+                    put4(sB, o, make_float4(xb[m].x * inv.x, xb[m].y * inv.y, xb[m].z * inv.z, xb[m].w * inv.w));
+                }
             }
         } else {
         // ---- inputs of the chunk into LDS (the last chunk is there already)
@@ -445,9 +461,15 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         {
             const int c = ltid & 7, seg = (ltid >> 3) & 7, j = (ltid >> 6) * 8 + c;
             const int ln = ltid & 63;
+            float wseg[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                wseg[u] = sG[sw(seg * 8 + u, j)];
+                if constexpr (kFused) wseg[u] = decay_from_pre(wseg[u]);
+            }
             float pr = 1.f;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) pr *= sG[sw(seg * 8 + u, j)];
+            for (int u = 0; u < 8; ++u) pr *= wseg[u];
             float inc = pr;   // product over segments 0 .. seg
 #pragma unroll
             for (int d = 1; d < 8; d *= 2) {
@@ -462,7 +484,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int o = sw(seg * 8 + u, j);
-                const float wv = sG[o];
+                const float wv = wseg[u];
                 pre_ *= wv;
                 ok = ok && wv >= kWMin && wv <= 1.f && pre_ >= kGMin;
                 sG[o] = pre_;
@@ -482,12 +504,15 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             const float4 inv = make_float4(1.f / gm.x, 1.f / gm.y, 1.f / gm.z, 1.f / gm.w);
             float4 x = lds4(sR, o);
             put4(sR, o, make_float4(x.x * gm.x, x.y * gm.y, x.z * gm.z, x.w * gm.w));
-            x = lds4(sA, o);
-            put4(sA, o, make_float4(x.x * gp.x, x.y * gp.y, x.z * gp.z, x.w * gp.w));
             x = lds4(sK, o);
             put4(sK, o, make_float4(x.x * inv.x, x.y * inv.y, x.z * inv.z, x.w * inv.w));
-            x = lds4(sB, o);
-            put4(sB, o, make_float4(x.x * inv.x, x.y * inv.y, x.z * inv.z, x.w * inv.w));
+            float4 xa = lds4(sA, o), xb = lds4(sB, o);
+            if constexpr (kFused) {   // xa: kk, xb: gate; a = -kk, b = kk gate
+                xb = make_float4(xa.x * xb.x, xa.y * xb.y, xa.z * xb.z, xa.w * xb.w);
+                xa = make_float4(-xa.x, -xa.y, -xa.z, -xa.w);
+            }
+            put4(sA, o, make_float4(xa.x * gp.x, xa.y * gp.y, xa.z * gp.z, xa.w * gp.w));
+            put4(sB, o, make_float4(xb.x * inv.x, xb.y * inv.y, xb.z * inv.z, xb.w * inv.w));
         }
         }   // bf16 prologue
         {
@@ -850,8 +875,17 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             // ---- outputs db, dr, da, dw (dw: prefix over steps of
             // k dk + b db - r dr - a da), beside the pass-3 Grams rb kt^T, ab kt^T
             float pre16[17];
+            float gate[2][4];   // fused inputs: the gate at this lane's output steps
             auto outputs = [&](int k) {
                 if (k == 0) {
+                    if constexpr (kFused) {
+                        const BufRsrc rg = raw_buffer(p.b + vbase, vext * sizeof(TIn) / 4);
+#pragma unroll
+                        for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                gate[lt][i] = bload1<TIn>(rg, ((uint32_t)t0 + 16 * TB[lt] + 4 * g + i) * ustride + jw);
+                    }
                     // exclusive prefix of the 16 block sums of column jw (fixed order)
                     pre16[0] = 0.f;
 #pragma unroll
@@ -875,10 +909,21 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                     const float adA = sA[o] * XA[lt][i];
                     const float wdw = (cj + ex) - adA;
                     const uint32_t off = ooff(t);
-                    bstore(odb, off, XB[lt][i] * inv);
                     bstore(odr, off, XR[lt][i] * gt);
-                    bstore(oda, off, XA[lt][i] * gp);
-                    bstore(odw, off, wdw * gp * inv);
+                    if constexpr (kFused) {
+                        // a = -kk: kk from ab = a g_{t-1}; ln w from w = g_t / g_{t-1}
+                        const float rgp = __builtin_amdgcn_rcpf(gp);
+                        const float da_ = XA[lt][i] * gp, db_ = XB[lt][i] * inv;
+                        const float kk = -sA[o] * rgp;
+                        const float lw = __builtin_amdgcn_logf(gt * rgp) * kLn2;   // ln w
+                        bstore(odb, off, kk * db_);
+                        bstore(oda, off, fmaf(gate[lt][i], db_, -da_));
+                        bstore(odw, off, wdw * lw * (1.f + lw * (1.f / kDecayCoeff)));
+                    } else {
+                        bstore(odb, off, XB[lt][i] * inv);
+                        bstore(oda, off, XA[lt][i] * gp);
+                        bstore(odw, off, wdw * gp * inv);
+                    }
                     ex += f[lt][i];
                 }
             };
@@ -943,7 +988,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
     if (tid == 0) p.flags[bh] = sBad;
 }
 
-template <typename TIn>
+template <typename TIn, bool kFused>
 hipError_t launch_bwdc_t(const BwdLaunch &a, int *flags, hipStream_t stream)
 {
     BwdcArgs<TIn> p;
@@ -968,7 +1013,7 @@ hipError_t launch_bwdc_t(const BwdLaunch &a, int *flags, hipStream_t stream)
     p.T = a.T;
     p.H = a.H;
     p.nck = (int)((a.T + 63) / 64);
-    hipLaunchKernelGGL((wkv7_bwdc_kernel<TIn>), dim3((unsigned)(a.B * a.H)), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((wkv7_bwdc_kernel<TIn, kFused>), dim3((unsigned)(a.B * a.H)), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -981,8 +1026,11 @@ bool chunked_backward_supported(const BwdLaunch &a)
 
 hipError_t launch_backward_chunked(const BwdLaunch &a, int *flags, hipStream_t stream)
 {
-    return a.dtype == 0 ? launch_bwdc_t<float>(a, flags, stream)
-                        : launch_bwdc_t<uint16_t>(a, flags, stream);
+    if (a.fused)
+        return a.dtype == 0 ? launch_bwdc_t<float, true>(a, flags, stream)
+                            : launch_bwdc_t<uint16_t, true>(a, flags, stream);
+    return a.dtype == 0 ? launch_bwdc_t<float, false>(a, flags, stream)
+                        : launch_bwdc_t<uint16_t, false>(a, flags, stream);
 }
 
 }  // namespace wkv7

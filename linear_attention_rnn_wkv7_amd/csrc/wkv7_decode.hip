@@ -8,6 +8,10 @@
 // the state through registers once, with fully coalesced 16-byte accesses,
 // and keeps everything else in registers.
 //
+// With fused inputs the w, a, b slots hold the decay pre-activation omega,
+// the normalised key kk and the gate ag of the page's tm_pre_forward, and
+// the kernel forms w = exp(-c sigmoid(omega)), a = -kk, b = kk ag itself.
+//
 // One workgroup per (b, h), NT threads.  Thread t owns four consecutive
 // columns 4 (t mod TPR) .. of RPT rows, row m RPP + t / TPR for m < RPT, so
 // that pass m of the workgroup reads NT float4 = RPP whole rows, contiguous
@@ -42,7 +46,7 @@ __device__ __forceinline__ float dot4(float4 x, float4 u)
     return fmaf(x.w, u.w, fmaf(x.z, u.z, fmaf(x.y, u.y, x.x * u.x)));
 }
 
-template <int N, typename TIn>
+template <int N, typename TIn, bool kFused>
 __global__ void __launch_bounds__(DecGeom<N>::NT) wkv7_decode_kernel(DecArgs<TIn> p)
 {
     using G = DecGeom<N>;
@@ -61,10 +65,16 @@ __global__ void __launch_bounds__(DecGeom<N>::NT) wkv7_decode_kernel(DecArgs<TIn
 #pragma unroll
         for (int m = 0; m < G::RPT; ++m) s[m] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    const float4 a4 = InQuad<TIn>::f32(InQuad<TIn>::load(p.a + vb + col));
-    const float4 w4 = InQuad<TIn>::f32(InQuad<TIn>::load(p.w + vb + col));
+    float4 a4 = InQuad<TIn>::f32(InQuad<TIn>::load(p.a + vb + col));
+    float4 w4 = InQuad<TIn>::f32(InQuad<TIn>::load(p.w + vb + col));
     const float4 k4 = InQuad<TIn>::f32(InQuad<TIn>::load(p.k + vb + col));
-    const float4 b4 = InQuad<TIn>::f32(InQuad<TIn>::load(p.b + vb + col));
+    float4 b4 = InQuad<TIn>::f32(InQuad<TIn>::load(p.b + vb + col));
+    if constexpr (kFused) {   // a4 holds kk, b4 the gate, w4 omega
+        b4 = make_float4(a4.x * b4.x, a4.y * b4.y, a4.z * b4.z, a4.w * b4.w);
+        a4 = make_float4(-a4.x, -a4.y, -a4.z, -a4.w);
+        w4 = make_float4(decay_from_pre(w4.x), decay_from_pre(w4.y), decay_from_pre(w4.z),
+                         decay_from_pre(w4.w));
+    }
     const float4 r4 = InQuad<TIn>::f32(InQuad<TIn>::load(p.r + vb + col));
     float vi[G::RPT];
 #pragma unroll
@@ -99,7 +109,7 @@ __global__ void __launch_bounds__(DecGeom<N>::NT) wkv7_decode_kernel(DecArgs<TIn
     }
 }
 
-template <int N, typename TIn>
+template <int N, typename TIn, bool kFused>
 hipError_t launch_dec_t(const FwdLaunch &a, hipStream_t stream)
 {
     DecArgs<TIn> p;
@@ -114,8 +124,8 @@ hipError_t launch_dec_t(const FwdLaunch &a, hipStream_t stream)
     p.sT = a.sT;
     p.ckpt = a.ckpt;
     p.sa = a.satape;
-    hipLaunchKernelGGL((wkv7_decode_kernel<N, TIn>), dim3((unsigned)(a.B * a.H)), dim3(DecGeom<N>::NT),
-                       0, stream, p);
+    hipLaunchKernelGGL((wkv7_decode_kernel<N, TIn, kFused>), dim3((unsigned)(a.B * a.H)),
+                       dim3(DecGeom<N>::NT), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -123,9 +133,14 @@ hipError_t launch_dec_t(const FwdLaunch &a, hipStream_t stream)
 
 hipError_t launch_decode(const FwdLaunch &a, hipStream_t stream)
 {
+    if (a.fused)   // N = 64 only (checked by the caller)
+        return a.dtype == 0 ? launch_dec_t<64, float, true>(a, stream)
+                            : launch_dec_t<64, uint16_t, true>(a, stream);
     if (a.N == 64)
-        return a.dtype == 0 ? launch_dec_t<64, float>(a, stream) : launch_dec_t<64, uint16_t>(a, stream);
-    return a.dtype == 0 ? launch_dec_t<16, float>(a, stream) : launch_dec_t<16, uint16_t>(a, stream);
+        return a.dtype == 0 ? launch_dec_t<64, float, false>(a, stream)
+                            : launch_dec_t<64, uint16_t, false>(a, stream);
+    return a.dtype == 0 ? launch_dec_t<16, float, false>(a, stream)
+                        : launch_dec_t<16, uint16_t, false>(a, stream);
 }
 
 }  // namespace wkv7

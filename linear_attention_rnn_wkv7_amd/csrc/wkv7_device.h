@@ -62,6 +62,21 @@ __device__ __forceinline__ float swap_add16(float x, float y)
     return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
 }
 
+// The decay the Foundry page forms from its pre-activation omega in
+// tm_pre_forward: w = exp(-c sigmoid(omega)), c = RX_WDECAY_COEFF = exp(-0.5).
+// omega = -inf gives w = 1 (used to pad past the end of a sequence).
+// Written with the hardware base-2 exponential and reciprocal (exp(x) =
+// 2^(x log2 e); each within a few ulp): sigmoid(omega) = 1 / (1 +
+// 2^(-omega log2 e)), w = 2^(-c log2(e) sigmoid(omega)).
+constexpr float kDecayCoeff = 0.606530659712633424f;
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLn2 = 0.693147180559945309f;
+__device__ __forceinline__ float decay_from_pre(float omega)
+{
+    const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * omega));
+    return __builtin_amdgcn_exp2f((-kDecayCoeff * kLog2e) * sg);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
 
@@ -105,6 +120,16 @@ __device__ __forceinline__ uint2 bload2(BufRsrc r, uint32_t off)
     typedef unsigned u2 __attribute__((ext_vector_type(2)));
     const u2 q = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
     return make_uint2(q.x, q.y);
+}
+
+// One input element at element offset `elem` of a buffer, widened to fp32.
+template <typename TIn>
+__device__ __forceinline__ float bload1(BufRsrc r, uint32_t elem)
+{
+    if constexpr (sizeof(TIn) == 4)
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)(elem * 4), 0, 0));
+    else
+        return bf16_lo(__builtin_amdgcn_raw_buffer_load_b16(r, (int)(elem * 2), 0, 0));
 }
 
 // 4 consecutive input elements, loaded raw (fp32: 16 bytes, bf16: 8 bytes)

@@ -281,6 +281,7 @@ hipError_t launch_fwd_t(const FwdLaunch &a, hipStream_t stream)
 hipError_t launch_forward(const FwdLaunch &a, hipStream_t stream)
 {
     if (a.T == 1) return launch_decode(a, stream);
+    if (a.fused && !forward_chunked_supported(a)) return hipErrorInvalidValue;   // checked by the caller
     if (a.N == 64) {
         if (forward_chunked_supported(a)) return launch_forward_chunked(a, stream);
         return a.dtype == 0 ? launch_fwd_t<64, float>(a, stream)

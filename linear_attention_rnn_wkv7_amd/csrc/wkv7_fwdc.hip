@@ -28,8 +28,12 @@
 // steps are done; Y: the state after the block is in LDS).  Blocks whose
 // decays leave [1/16, 1] or whose cumulative decay drops below 2^-60, and a
 // final partial block, run the plain step on the scan waves instead (y on
-// the VALU, no rescaling).  Checkpoints must fall on block starts (chunk a
-// multiple of 32).
+// the VALU, no rescaling).  With fused inputs the w, a, b slots hold the
+// decay pre-activation omega, the normalised key kk and the gate ag of the
+// page's tm_pre_forward; the kernel forms w = exp(-c sigmoid(omega)),
+// a = -kk and b = kk ag where it first reads them (the decay's cumulative
+// product, the rescaling pass, the plain steps).  Checkpoints must fall on
+// block starts (chunk a multiple of 32).
 
 #include <type_traits>
 
@@ -100,7 +104,7 @@ struct FwdcArgs {
     int chunk, nck;
 };
 
-template <typename TIn>
+template <typename TIn, bool kFused>
 __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
 {
     constexpr int N = 64, R = 2, CC = 8, LPR = 8;
@@ -243,6 +247,14 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                     row8(L + vK * kTB * N, s, kv);
                     row8(L + vB * kTB * N, s, bv);
                     row8(L + vR * kTB * N, s, rv);
+                    if constexpr (kFused) {   // av: kk, bv: gate, wv: omega
+#pragma unroll
+                        for (int c = 0; c < CC; ++c) {
+                            bv[c] = av[c] * bv[c];
+                            av[c] = -av[c];
+                            wv[c] = decay_from_pre(wv[c]);
+                        }
+                    }
                     float sa[R], yv[R];
 #pragma unroll
                     for (int e = 0; e < R; ++e) {
@@ -411,7 +423,10 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                 if (ok) {
                     float wv[8];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) wv[u] = sb[vW * 2048 + L3 + 256 * u + 16 * (h ^ (u & 3))];
+                    for (int u = 0; u < 8; ++u) {
+                        wv[u] = sb[vW * 2048 + L3 + 256 * u + 16 * (h ^ (u & 3))];
+                        if constexpr (kFused) wv[u] = decay_from_pre(wv[u]);
+                    }
                     float G = 1.f;   // product over the steps before 4 u
 #pragma unroll
                     for (int u = 0; u < 8; ++u) {
@@ -437,9 +452,15 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                 const float4 iv = make_float4(__builtin_amdgcn_rcpf(gt.x), __builtin_amdgcn_rcpf(gt.y),
                                               __builtin_amdgcn_rcpf(gt.z), __builtin_amdgcn_rcpf(gt.w));
                 put4(sb + vR * 2048, Lr, make_float4(x0.x * gt.x, x0.y * gt.y, x0.z * gt.z, x0.w * gt.w));
-                put4(sb + vA * 2048, Lr, make_float4(x1.x * gp.x, x1.y * gp.y, x1.z * gp.z, x1.w * gp.w));
                 put4(sb + vK * 2048, Lr, make_float4(x2.x * iv.x, x2.y * iv.y, x2.z * iv.z, x2.w * iv.w));
-                put4(sb + vB * 2048, Lr, make_float4(x3.x * iv.x, x3.y * iv.y, x3.z * iv.z, x3.w * iv.w));
+                if constexpr (kFused) {   // x1: kk, x3: gate; a = -kk, b = kk gate
+                    put4(sb + vA * 2048, Lr, make_float4(-x1.x * gp.x, -x1.y * gp.y, -x1.z * gp.z, -x1.w * gp.w));
+                    put4(sb + vB * 2048, Lr, make_float4(x1.x * x3.x * iv.x, x1.y * x3.y * iv.y,
+                                                         x1.z * x3.z * iv.z, x1.w * x3.w * iv.w));
+                } else {
+                    put4(sb + vA * 2048, Lr, make_float4(x1.x * gp.x, x1.y * gp.y, x1.z * gp.z, x1.w * gp.w));
+                    put4(sb + vB * 2048, Lr, make_float4(x3.x * iv.x, x3.y * iv.y, x3.z * iv.z, x3.w * iv.w));
+                }
                 if (h == kNH - 1 && tr == kTB - 1) put4(g31[b], 4 * cq, gt);
             }
             return fast;
@@ -662,7 +683,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
     }
 }
 
-template <typename TIn>
+template <typename TIn, bool kFused>
 hipError_t launch_fwdc_t(const FwdLaunch &a, hipStream_t stream)
 {
     FwdcArgs<TIn> p;
@@ -676,7 +697,8 @@ hipError_t launch_fwdc_t(const FwdLaunch &a, hipStream_t stream)
     p.H = a.H;
     p.chunk = a.chunk;
     p.nck = (int)((a.T + a.chunk - 1) / a.chunk);
-    hipLaunchKernelGGL((wkv7_fwdc_kernel<TIn>), dim3((unsigned)(a.B * a.H)), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((wkv7_fwdc_kernel<TIn, kFused>), dim3((unsigned)(a.B * a.H)), dim3(kThreads), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -689,7 +711,9 @@ bool forward_chunked_supported(const FwdLaunch &a)
 
 hipError_t launch_forward_chunked(const FwdLaunch &a, hipStream_t stream)
 {
-    return a.dtype == 0 ? launch_fwdc_t<float>(a, stream) : launch_fwdc_t<uint16_t>(a, stream);
+    if (a.fused)
+        return a.dtype == 0 ? launch_fwdc_t<float, true>(a, stream) : launch_fwdc_t<uint16_t, true>(a, stream);
+    return a.dtype == 0 ? launch_fwdc_t<float, false>(a, stream) : launch_fwdc_t<uint16_t, false>(a, stream);
 }
 
 }  // namespace wkv7

@@ -19,6 +19,7 @@ struct FwdLaunch {
     int64_t B, T, H, N;
     int dtype;               // 0 f32, 1 bf16
     int chunk;               // checkpoint interval
+    int fused;               // w, a, b slots hold omega, kk, gate (N = 64)
 };
 
 struct BwdLaunch {
@@ -34,6 +35,7 @@ struct BwdLaunch {
     int dtype;
     int chunk;
     int algo;                // wkv7_algo
+    int fused;               // as FwdLaunch; the chunk form only
 };
 
 // The chunk forms address one (b) slice of a [B][T][H][64] tensor with

@@ -26,11 +26,11 @@ def test_exports_every_declared_symbol():
     assert declared == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.wkv7_abi_version() == 102
+    assert L.wkv7_abi_version() == 103
 
 
-def _shape(B=2, T=10, H=3, N=64, dtype=0, chunk=64, algo=0, reserved=0):
-    return _lib.Shape(B, T, H, N, dtype, chunk, algo, reserved)
+def _shape(B=2, T=10, H=3, N=64, dtype=0, chunk=64, algo=0, flags=0):
+    return _lib.Shape(B, T, H, N, dtype, chunk, algo, flags)
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
@@ -90,7 +90,18 @@ def test_backward_validation():
     assert _bwd(_shape(N=16, dtype=5)) == _lib.WKV7_ERR_INVALID
     assert _bwd(_shape(algo=3)) == _lib.WKV7_ERR_INVALID
     assert _bwd(_shape(algo=-1)) == _lib.WKV7_ERR_INVALID
-    assert _bwd(_shape(reserved=1)) == _lib.WKV7_ERR_INVALID
+    assert _bwd(_shape(flags=2)) == _lib.WKV7_ERR_INVALID
+    assert _bwd(_shape(flags=-1)) == _lib.WKV7_ERR_INVALID
+    # fused inputs: the chunk form's shapes only (N = 64, C = 64, not SCAN)
+    F = _lib.WKV7_FUSED_INPUTS
+    assert _bwd(_shape(flags=F, N=16)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert _bwd(_shape(flags=F, chunk=32)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert _bwd(_shape(flags=F, algo=1)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert _bwd(_shape(flags=F, B=1, T=(1 << 31) // 256, H=1)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert _bwd(_shape(flags=F)) == _lib.WKV7_ERR_WORKSPACE   # valid: fails on the workspace
+    assert _fwd(_shape(flags=F, N=16)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert _fwd(_shape(flags=F, chunk=128)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert _fwd(_shape(flags=2)) == _lib.WKV7_ERR_INVALID
     # the chunk form needs N = 64 and C = 64
     assert _bwd(_shape(N=16, algo=2)) == _lib.WKV7_ERR_UNSUPPORTED
     assert _bwd(_shape(chunk=32, algo=2)) == _lib.WKV7_ERR_UNSUPPORTED
