@@ -59,6 +59,28 @@ def test_parity_sampled_full_size(name):
     _check(got, ref, H.TAU[inp["r"].dtype], name)
 
 
+@pytest.mark.parametrize("T,algo", [(131071, "chunked"), (131072, "auto")],
+                         ids=["chunk_form_at_offset_limit", "step_scan_past_limit"])
+def test_offset_limit(T, algo):
+    """One batch row of a vector tensor just below 2^31 bytes (B = 1, H = 64,
+    T * H * 64 * 4 = 2^31 - 16 KiB) runs the chunk form with its 32-bit
+    buffer offsets (forced: it must apply); at 2^31 bytes the chunk form no
+    longer applies and the step scan takes every head.  Tensors of 2 GiB
+    each; sampled whole recurrences against the oracle."""
+    wl = custom(1, T, 64, 64, "f32", True, True, seed=71)
+    _say(f"case offset limit T={T} algo={algo}")
+    inp = make_inputs(wl, device="cuda")
+    out = H.gpu_run(inp, algo=algo)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (0, 63)]
+    got = H.gpu_pairs(out, pairs)
+    del out
+    ref = H.oracle_run(inp, pairs=pairs)
+    del inp
+    torch.cuda.empty_cache()
+    _check(got, ref, 2e-4, f"offset limit T={T}")
+
+
 EDGE = [
     # (B, T, H, N, dtype, s0, dsT, chunk)
     (1, 1, 1, 64, "f32", True, True, 64),
