@@ -225,8 +225,8 @@ def cpu_baseline(inp, wl, budget_s, fused=False):
             [c64(state_slice(inp["dsT"], b, h)) for b, h in pairs], 1)
         return sl, s0, dsT
 
-    def run(pairs):
-        sl, s0, dsT = sample(pairs)
+    def run(pairs, data=None):
+        sl, s0, dsT = data if data is not None else sample(pairs)
         threads = min(cores, len(pairs))
         t = time.perf_counter()
         orc = oracle.fused if fused else oracle
@@ -239,15 +239,21 @@ def cpu_baseline(inp, wl, budget_s, fused=False):
     # one pair per core per round; as many pairs as fit the time budget
     n = int(max(1, min(len(all_pairs), cores * max(1, int(budget_s / max(probe_t, 1e-3))))))
     pairs = all_pairs[:n]
-    dt, threads = run(pairs)
-    token_heads = len(pairs) * wl.T
+    # whole passes over the sample until the budget is spent (at least one)
+    data = sample(pairs)
+    dt, passes = 0.0, 0
+    while passes == 0 or dt < 0.6 * budget_s:
+        t, threads = run(pairs, data)
+        dt += t
+        passes += 1
+    token_heads = passes * len(pairs) * wl.T
     return {
         "value": token_heads / dt / wl.H,
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{len(pairs)} of {wl.B * wl.H} whole (b,h) recurrences (T={wl.T}), "
-                  f"fp64 fwd+bwd in {dt:.1f} s; tokens/s = token-heads/s / H",
+        "sample": f"{len(pairs)} of {wl.B * wl.H} whole (b,h) recurrences (T={wl.T}) x {passes} "
+                  f"passes, fp64 fwd+bwd in {dt:.1f} s; tokens/s = token-heads/s / H",
     }
 
 
