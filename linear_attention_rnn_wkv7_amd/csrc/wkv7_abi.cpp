@@ -14,8 +14,32 @@ constexpr size_t kAlign = 256;   // workspace sub-buffer alignment
 struct Dims {
     int64_t B, T, H, N, C, nck;
     int dtype, algo, fused;
+    int nseg, nckseg;                // sequence split (nseg = 1: none)
     size_t vec_elems, state_elems;   // per tensor
 };
+
+// Few, long sequences run in segments so that more workgroups than (b, h)
+// pairs fill the device: up to 8 segments of at least 8 chunks, while there
+// are at most 64 (b, h).  Needs the chunk forms (N = 64, C = 64).  Depends on
+// the shape only, so the forward's checkpoint record and the backward agree.
+void plan_split(Dims *d)
+{
+    d->nseg = 1;
+    d->nckseg = (int)d->nck;
+    const int64_t units = d->B * d->H;
+    if (d->N != 64 || d->C != 64 || d->T <= 1 || units == 0 || units > 64 ||
+        !wkv7::chunk_offsets_fit(d->T, d->H))
+        return;
+    int64_t nseg = 256 / units;
+    if (nseg > 8) nseg = 8;
+    if (nseg > d->nck / 8) nseg = d->nck / 8;
+    if (nseg < 2) return;
+    const int64_t per = (d->nck + nseg - 1) / nseg;
+    nseg = (d->nck + per - 1) / per;   // no empty segment
+    if (nseg < 2) return;
+    d->nseg = (int)nseg;
+    d->nckseg = (int)per;
+}
 
 bool mul_ok(int64_t a, int64_t b, int64_t *out)
 {
@@ -51,6 +75,7 @@ int check_shape(const wkv7_shape *s, Dims *d)
     d->fused = (s->flags & WKV7_FUSED_INPUTS) != 0;
     d->vec_elems = (size_t)vec;
     d->state_elems = (size_t)st;
+    plan_split(d);
     return WKV7_OK;
 }
 
@@ -79,9 +104,25 @@ size_t ckpt_state_bytes(const Dims &d)
     return d.state_elems * (size_t)d.nck * sizeof(float);
 }
 
+// A split sequence's record also holds the segments' transition products,
+// after the tape: [B*H][nseg][N][N] fp32.
+size_t ckpt_split_bytes(const Dims &d)
+{
+    return d.nseg > 1 ? (size_t)(d.B * d.H) * d.nseg * d.N * d.N * sizeof(float) : 0;
+}
+
 size_t ckpt_bytes(const Dims &d)
 {
-    return round_up(ckpt_state_bytes(d)) + d.vec_elems * sizeof(float);
+    const size_t tape = d.vec_elems * sizeof(float);
+    if (d.nseg > 1) return round_up(ckpt_state_bytes(d)) + round_up(tape) + ckpt_split_bytes(d);
+    return round_up(ckpt_state_bytes(d)) + tape;
+}
+
+float *pbuf_of(const float *ck, const Dims &d)
+{
+    return reinterpret_cast<float *>(const_cast<char *>(reinterpret_cast<const char *>(ck)) +
+                                     round_up(ckpt_state_bytes(d)) +
+                                     round_up(d.vec_elems * sizeof(float)));
 }
 
 const float *tape_of(const float *ck, const Dims &d)
@@ -102,9 +143,18 @@ size_t flag_region(const Dims &d)
     return round_up((size_t)(d.B * d.H) * sizeof(int));
 }
 
+// split sequences: per-segment flags, then the state gradients at segment
+// starts ([B*H][nseg][N][N] fp32)
+size_t split_region(const Dims &d)
+{
+    if (d.nseg < 2) return 0;
+    return round_up((size_t)(d.B * d.H) * d.nseg * sizeof(int)) +
+           round_up((size_t)(d.B * d.H) * d.nseg * d.N * d.N * sizeof(float));
+}
+
 size_t workspace_bytes(const Dims &d, bool ckpt_provided)
 {
-    size_t n = sub_region(d) + flag_region(d);
+    size_t n = sub_region(d) + flag_region(d) + split_region(d);
     if (!ckpt_provided) n += round_up(ckpt_bytes(d));
     return n;
 }
@@ -167,6 +217,11 @@ int wkv7_forward(const wkv7_shape *shape, const void *r, const void *w, const vo
     L.dtype = d.dtype;
     L.chunk = (int)d.C;
     L.fused = d.fused;
+    if (ckpt && d.nseg > 1) {   // the record holds the split's scratch
+        L.nseg = d.nseg;
+        L.nckseg = d.nckseg;
+        L.pbuf = pbuf_of(ckpt, d);
+    }
     return hip_status(wkv7::launch_forward(L, stream));
 }
 
@@ -211,7 +266,7 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
     float *sub = reinterpret_cast<float *>(ws);
     const float *ck = ckpt;
     if (!ckpt) {
-        float *own = reinterpret_cast<float *>(ws + sub_region(d) + flag_region(d));
+        float *own = reinterpret_cast<float *>(ws + sub_region(d) + flag_region(d) + split_region(d));
         wkv7::FwdLaunch F;
         for (int i = 0; i < 6; ++i) F.in[i] = in[i];
         F.s0 = s0;
@@ -226,6 +281,11 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
         F.dtype = d.dtype;
         F.chunk = (int)d.C;
         F.fused = d.fused;
+        if (d.nseg > 1) {
+            F.nseg = d.nseg;
+            F.nckseg = d.nckseg;
+            F.pbuf = pbuf_of(own, d);
+        }
         rc = hip_status(wkv7::launch_forward(F, stream));
         if (rc != WKV7_OK) return rc;
         ck = own;
@@ -247,6 +307,14 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
     L.chunk = (int)d.C;
     L.algo = d.algo;
     L.fused = d.fused;
+    if (d.nseg > 1) {
+        char *sp = ws + sub_region(d) + flag_region(d);
+        L.nseg = d.nseg;
+        L.nckseg = d.nckseg;
+        L.pbuf = pbuf_of(ck, d);
+        L.unit_flags = reinterpret_cast<int *>(sp);
+        L.gbuf = reinterpret_cast<float *>(sp + round_up((size_t)(d.B * d.H) * d.nseg * sizeof(int)));
+    }
     return hip_status(wkv7::launch_backward(L, stream));
 }
 

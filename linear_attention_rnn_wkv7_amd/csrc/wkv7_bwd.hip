@@ -501,15 +501,24 @@ size_t sub_bytes(int64_t B, int64_t H, int64_t N, int chunk)
 hipError_t launch_backward(const BwdLaunch &a, hipStream_t stream)
 {
     const int *only = nullptr;
-    if (a.fused) {
-        // the decays formed from fused inputs lie in [exp(-exp(-0.5)), 1]: the
-        // chunk form takes every head (the caller checked that it applies)
-        if (!chunked_backward_supported(a)) return hipErrorInvalidValue;
-        return launch_backward_chunked(a, a.flags, stream);
-    }
-    if (a.algo != 1 && chunked_backward_supported(a)) {
-        const hipError_t e = launch_backward_chunked(a, a.flags, stream);
+    const bool chunked = a.algo != 1 && chunked_backward_supported(a);
+    if (a.fused && !chunked) return hipErrorInvalidValue;   // checked by the caller
+    if (chunked && a.nseg > 1) {
+        // a split sequence: the later segments with their own gradients
+        // only, the carries, then the earlier segments with their incoming
+        // gradients; a head with any flagged segment is redone whole below
+        hipError_t e = launch_backward_chunked(a, a.unit_flags, 1, stream);
+        if (e == hipSuccess) e = launch_compose_backward(a, stream);
+        if (e == hipSuccess) e = launch_backward_chunked(a, a.unit_flags, 2, stream);
+        if (e != hipSuccess || a.fused) return e;
+        e = launch_flag_reduce(a.unit_flags, a.flags, a.B * a.H, a.nseg, stream);
         if (e != hipSuccess) return e;
+        only = a.flags;
+    } else if (chunked) {
+        const hipError_t e = launch_backward_chunked(a, a.flags, 0, stream);
+        // the decays formed from fused inputs lie in [exp(-exp(-0.5)), 1]:
+        // the chunk form takes every head
+        if (e != hipSuccess || a.fused) return e;
         only = a.flags;
     }
     if (a.N == 64)

@@ -205,6 +205,13 @@ struct BwdcArgs {
     int *flags;
     int64_t T, H;
     int nck;
+    // sequence split: mode 0 runs whole (b, h) sequences (one workgroup per
+    // (b, h)); mode 1 (first pass) the segments s = 1 .. nseg - 1 of nckseg
+    // chunks each, with zero incoming gradient except the last and dL/d(the
+    // segment's initial state) to gbuf; mode 2 (second pass) the segments
+    // s = 0 .. nseg - 2 with the incoming gradient from gbuf[s + 1].
+    int mode, nseg, nckseg;
+    float *gbuf;   // [B*H][nseg][64][64]
 };
 
 // x from the lane of row-group G0 (lane >> 4 == G0) with the same lane & 15,
@@ -243,11 +250,33 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int fb = wave & 3, half = wave >> 2;
-    const int64_t bh = blockIdx.x, T = p.T, H = p.H;
+    const int64_t T = p.T, H = p.H;
+    const int nck = p.nck;
+    // this workgroup's (b, h), chunk range [cb, ce), incoming state gradient
+    // and where dL/d(initial state) goes
+    int64_t bh = blockIdx.x;
+    int seg = 0, cb = 0, ce = nck;
+    const float *dsTu = p.dsT ? p.dsT + bh * 4096 : nullptr;
+    float *ds0u = p.ds0 ? p.ds0 + bh * 4096 : nullptr;
+    int64_t fidx = bh;
+    if (p.mode != 0) {
+        const int per = p.nseg - 1;
+        bh = (int64_t)blockIdx.x / per;
+        seg = (int)((int64_t)blockIdx.x % per) + (p.mode == 1 ? 1 : 0);
+        cb = seg * p.nckseg;
+        ce = cb + p.nckseg < nck ? cb + p.nckseg : nck;
+        fidx = bh * p.nseg + seg;
+        if (p.mode == 1) {
+            dsTu = seg == p.nseg - 1 && p.dsT ? p.dsT + bh * 4096 : nullptr;
+            ds0u = p.gbuf + fidx * 4096;
+        } else {
+            dsTu = p.gbuf + (fidx + 1) * 4096;
+            ds0u = seg == 0 && p.ds0 ? p.ds0 + bh * 4096 : nullptr;
+        }
+    }
     const int64_t bidx = bh / H, head = bh % H;
     const int64_t stride = H * 64;
     const int64_t vbase = (bidx * T * H + head) * 64;
-    const int nck = p.nck;
     // bytes of this (b, h)'s steps in a [B][T][H][64] tensor, from step 0:
     // buffer accesses past them (the tail of a partial last chunk) read
     // zeros and drop stores
@@ -272,7 +301,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
     for (int lb = 0; lb < 2; ++lb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            Hc[lb][i] = p.dsT ? p.dsT[bh * 4096 + (16 * g + 4 * (2 * half + lb) + i) * 64 + jw] : 0.f;
+            Hc[lb][i] = dsTu ? dsTu[(16 * g + 4 * (2 * half + lb) + i) * 64 + jw] : 0.f;
     if (tid == 0) sBad = 0;
 
     // The inputs of a chunk (r, w, k, a, b, v, dy) and its checkpoint's
@@ -379,7 +408,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         if (!gok) sBad = 1;   // every writer stores 1
     };
     {
-        const int cl = nck - 1, Ll = chunk_len(cl);
+        const int cl = ce - 1, Ll = chunk_len(cl);
 #pragma unroll
         for (int q = 0; q < 7; ++q)
             if (!kDma || q != 1) issue_regs(cl, q);
@@ -400,7 +429,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         }
     }
 
-    for (int c = nck - 1; c >= 0; --c) {
+    for (int c = ce - 1; c >= cb; --c) {
         const int64_t t0 = (int64_t)c * 64;
         const int Lc = chunk_len(c);
 
@@ -447,7 +476,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             }
         } else {
         // ---- inputs of the chunk into LDS (the last chunk is there already)
-        if (c != nck - 1) {
+        if (c != ce - 1) {
 #pragma unroll
             for (int q = 0; q < 7; ++q) commit_regs(64, q);
         }
@@ -526,7 +555,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
         __syncthreads();
         refresh();
         // the next chunk's decay factors, read now, formed during this chunk
-        if (kDma && c > 0) load_w(c - 1);
+        if (kDma && c > cb) load_w(c - 1);
         // Hb column jw (rows 16 g + s) and row jw (columns 16 g + s): the B
         // operands of its phase-2 products
         float hB[16], hR[16];
@@ -748,17 +777,17 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                 cp = swap_add16(cp, cp);
                 cp = swap_add32(cp, cp);
                 if (g == 0) sCj[HF][jw] = cp;
-                if (c == 0 && p.ds0) {
+                if (c == cb && ds0u) {
 #pragma unroll
                     for (int lb = 0; lb < 2; ++lb)
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            p.ds0[bh * 4096 + (16 * g + 4 * (2 * HF + lb) + i) * 64 + jw] = Hn[lb][i];
+                            ds0u[(16 * g + 4 * (2 * HF + lb) + i) * 64 + jw] = Hn[lb][i];
                 }
 #pragma unroll
                 for (int lb = 0; lb < 2; ++lb) Hc[lb] = Hn[lb];
             }
-            if (c > 0) issue_s0(c - 1);   // this chunk's S0 column is no longer needed
+            if (c > cb) issue_s0(c - 1);   // this chunk's S0 column is no longer needed
             // sa for the second pass, loaded while the first one runs
             float4 saR[2];
 #pragma unroll
@@ -864,7 +893,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             __syncthreads();
             refresh();
             // next chunk: v (sa is done with) and, through registers, k and dy
-            if (c > 0) {
+            if (c > cb) {
 #pragma unroll
                 for (int q = 0; q < 7; ++q) {
                     if (kDma && q == 5) issue_dma(c - 1, q);
@@ -931,7 +960,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             __syncthreads();
             refresh();
             // next chunk: r, w, a, b straight into their (now free) arrays
-            if (kDma && c > 0) {
+            if (kDma && c > cb) {
                 issue_dma(c - 1, 0);
                 issue_dma(c - 1, 3);
                 issue_dma(c - 1, 4);
@@ -969,7 +998,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             // the next chunk's copies land before the barrier that publishes
             // them; the wait (for every earlier memory operation of the wave)
             // comes before dv's stores, so that it does not wait for them
-            if (kDma && c > 0) wait_dma();
+            if (kDma && c > cb) wait_dma();
 #pragma unroll
             for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
@@ -985,11 +1014,11 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
     }
 
     __syncthreads();
-    if (tid == 0) p.flags[bh] = sBad;
+    if (tid == 0) p.flags[fidx] = sBad;
 }
 
 template <typename TIn, bool kFused>
-hipError_t launch_bwdc_t(const BwdLaunch &a, int *flags, hipStream_t stream)
+hipError_t launch_bwdc_t(const BwdLaunch &a, int *flags, int mode, hipStream_t stream)
 {
     BwdcArgs<TIn> p;
     p.r = static_cast<const TIn *>(a.in[0]);
@@ -1013,7 +1042,12 @@ hipError_t launch_bwdc_t(const BwdLaunch &a, int *flags, hipStream_t stream)
     p.T = a.T;
     p.H = a.H;
     p.nck = (int)((a.T + 63) / 64);
-    hipLaunchKernelGGL((wkv7_bwdc_kernel<TIn, kFused>), dim3((unsigned)(a.B * a.H)), dim3(512), 0, stream, p);
+    p.mode = mode;
+    p.nseg = a.nseg;
+    p.nckseg = a.nckseg;
+    p.gbuf = a.gbuf;
+    const int64_t units = mode == 0 ? a.B * a.H : a.B * a.H * (a.nseg - 1);
+    hipLaunchKernelGGL((wkv7_bwdc_kernel<TIn, kFused>), dim3((unsigned)units), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1024,13 +1058,13 @@ bool chunked_backward_supported(const BwdLaunch &a)
     return a.N == 64 && a.chunk == 64 && chunk_offsets_fit(a.T, a.H);
 }
 
-hipError_t launch_backward_chunked(const BwdLaunch &a, int *flags, hipStream_t stream)
+hipError_t launch_backward_chunked(const BwdLaunch &a, int *flags, int mode, hipStream_t stream)
 {
     if (a.fused)
-        return a.dtype == 0 ? launch_bwdc_t<float, true>(a, flags, stream)
-                            : launch_bwdc_t<uint16_t, true>(a, flags, stream);
-    return a.dtype == 0 ? launch_bwdc_t<float, false>(a, flags, stream)
-                        : launch_bwdc_t<uint16_t, false>(a, flags, stream);
+        return a.dtype == 0 ? launch_bwdc_t<float, true>(a, flags, mode, stream)
+                            : launch_bwdc_t<uint16_t, true>(a, flags, mode, stream);
+    return a.dtype == 0 ? launch_bwdc_t<float, false>(a, flags, mode, stream)
+                        : launch_bwdc_t<uint16_t, false>(a, flags, mode, stream);
 }
 
 }  // namespace wkv7

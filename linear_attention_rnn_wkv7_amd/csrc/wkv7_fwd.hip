@@ -283,7 +283,13 @@ hipError_t launch_forward(const FwdLaunch &a, hipStream_t stream)
     if (a.T == 1) return launch_decode(a, stream);
     if (a.fused && !forward_chunked_supported(a)) return hipErrorInvalidValue;   // checked by the caller
     if (a.N == 64) {
-        if (forward_chunked_supported(a)) return launch_forward_chunked(a, stream);
+        if (a.nseg > 1) {   // a split sequence (the caller checked that the chunk form applies)
+            hipError_t e = launch_forward_chunked(a, 1, stream);
+            if (e == hipSuccess) e = launch_compose_forward(a, stream);
+            if (e == hipSuccess) e = launch_forward_chunked(a, 2, stream);
+            return e;
+        }
+        if (forward_chunked_supported(a)) return launch_forward_chunked(a, 0, stream);
         return a.dtype == 0 ? launch_fwd_t<64, float>(a, stream)
                             : launch_fwd_t<64, uint16_t>(a, stream);
     }

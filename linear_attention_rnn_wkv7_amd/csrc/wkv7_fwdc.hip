@@ -102,6 +102,15 @@ struct FwdcArgs {
     float *y, *sT, *ckpt, *sa;
     int64_t T, H;
     int chunk, nck;
+    // sequence split (segments of nckseg checkpoint intervals): mode 0 runs
+    // whole (b, h) sequences; mode 1 runs, per (b, h), the segments
+    // s = 0 .. nseg - 2 from zero (s0 for s = 0) to their end state Q_s
+    // (into the checkpoint at the next segment's start), then s = 1 .. nseg - 2
+    // with v = 0 from the identity, giving the segment's transition product
+    // P_s (into pbuf), and writes nothing else; mode 2 runs every segment
+    // from its carry-in state (the checkpoint at its start) with all outputs.
+    int mode, nseg, nckseg;
+    float *pbuf;   // [B*H][nseg][64][64]
 };
 
 template <typename TIn, bool kFused>
@@ -120,10 +129,45 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t bh = blockIdx.x, T = p.T, H = p.H;
+    const int64_t H = p.H;
+    // this workgroup's (b, h) and steps [tb0, tb0 + T) of its sequence, its
+    // initial state (s0u; or the identity), where its final state goes, and
+    // whether it writes y, the sa tape and the checkpoints
+    int64_t bh = blockIdx.x, tb0 = 0, T = p.T;
+    const float *s0u = p.s0 ? p.s0 + bh * N * N : nullptr;
+    float *sTu = p.sT ? p.sT + bh * N * N : nullptr;
+    bool s0_eye = false, zero_v = false, outs = true;
+    if (p.mode != 0) {
+        const int64_t Tseg = (int64_t)p.nckseg * p.chunk;
+        int seg;
+        if (p.mode == 1) {
+            const int per = 2 * p.nseg - 3, k = (int)((int64_t)blockIdx.x % per);
+            bh = (int64_t)blockIdx.x / per;
+            outs = false;
+            if (k < p.nseg - 1) {   // Q_s
+                seg = k;
+                s0u = seg == 0 && p.s0 ? p.s0 + bh * N * N : nullptr;
+                sTu = p.ckpt + (bh * p.nck + (int64_t)(seg + 1) * p.nckseg) * N * N;
+            } else {                // P_s
+                seg = k - (p.nseg - 1) + 1;
+                s0u = nullptr;
+                s0_eye = zero_v = true;
+                sTu = p.pbuf + (bh * p.nseg + seg) * N * N;
+            }
+        } else {
+            bh = (int64_t)blockIdx.x / p.nseg;
+            seg = (int)((int64_t)blockIdx.x % p.nseg);
+            s0u = seg == 0 ? (p.s0 ? p.s0 + bh * N * N : nullptr)
+                           : p.ckpt + (bh * p.nck + (int64_t)seg * p.nckseg) * N * N;
+            sTu = seg == p.nseg - 1 && p.sT ? p.sT + bh * N * N : nullptr;
+        }
+        tb0 = seg * Tseg;
+        T = p.T - tb0 < Tseg ? p.T - tb0 : Tseg;
+    }
+    float *const yp = outs ? p.y : nullptr;
     const int64_t bidx = bh / H, head = bh % H;
     const int64_t stride = H * N;
-    const int64_t vbase = (bidx * T * H + head) * N;
+    const int64_t vbase = (bidx * p.T * H + head) * N + tb0 * stride;
     const int64_t nblk = (T + kTB - 1) / kTB;
     auto steps_of = [&](int64_t blk) -> int {
         const int64_t rem = T - blk * kTB;
@@ -135,6 +179,8 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
         hbad[0] = hbad[1] = 0;
         hcnt = 0;
     }
+    if (zero_v)   // v is never staged: both slots read zeros
+        for (int i = tid; i < 2 * kTB * N; i += kThreads) slot[i / (kTB * N)][vV][i % (kTB * N)] = 0.f;
     __syncthreads();
 
     if (wave < 4) {
@@ -143,8 +189,13 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
         const int row0 = wave * 16 + rg * R, col0 = cg * CC;
 
         float S[R][CC];
-        if (p.s0) {
-            const float *src = p.s0 + bh * N * N + (int64_t)row0 * N + col0;
+        if (s0_eye) {
+#pragma unroll
+            for (int e = 0; e < R; ++e)
+#pragma unroll
+                for (int c = 0; c < CC; ++c) S[e][c] = row0 + e == col0 + c ? 1.f : 0.f;
+        } else if (s0u) {
+            const float *src = s0u + (int64_t)row0 * N + col0;
 #pragma unroll
             for (int e = 0; e < R; ++e)
 #pragma unroll
@@ -280,15 +331,15 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                         yv[e] = group_allreduce<LPR>(y0 + y1);
                     }
                     park(&SA[sw(s, row0 + cg)], sa);
-                    if (p.y && cg < R) p.y[vbase + (t0 + s) * stride + row0 + cg] = cg == 0 ? yv[0] : yv[1];
+                    if (yp && cg < R) yp[vbase + (t0 + s) * stride + row0 + cg] = cg == 0 ? yv[0] : yv[1];
                 }
                 __syncthreads();   // X
             }
             put_state();           // the state before block q + 1
             __syncthreads();       // Y
         }
-        if (p.sT) {
-            float *dst = p.sT + bh * N * N + (int64_t)row0 * N + col0;
+        if (sTu) {
+            float *dst = sTu + (int64_t)row0 * N + col0;
 #pragma unroll
             for (int e = 0; e < R; ++e)
 #pragma unroll
@@ -305,13 +356,13 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
     // offsets plus a constant, so that the helpers spend their issue slots
     // on loads, stores and MFMAs rather than on address arithmetic.
     const int l16 = lane & 15, g = lane >> 4, qa = l16 >> 2, c3 = l16 & 3;
-    const bool want_y = p.y != nullptr;
+    const bool want_y = yp != nullptr;
     const TIn *in_ptr[6];
 #pragma unroll
     for (int v = 0; v < 6; ++v) in_ptr[v] = p.in[v] + vbase;
-    float *const y_out = p.y ? p.y + vbase : nullptr;
-    float *const sa_out = p.sa ? p.sa + vbase : nullptr;
-    float *const ck_out = p.ckpt;
+    float *const y_out = yp ? yp + vbase : nullptr;
+    float *const sa_out = outs && p.sa ? p.sa + vbase : nullptr;
+    float *const ck_out = outs ? p.ckpt : nullptr;
     const int chunk = p.chunk, nck = p.nck;
     float *const gbuf = &gram[0][0];   // g of the block being rescaled
 
@@ -374,6 +425,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
         Raw pre[kU];
         auto stage_unit = [&](int64_t t0, int b, int k) {
             const int unit = kU * h + k, v = unit >> 3, u = unit & 7;
+            if (zero_v && v == vV) return;
             const TIn *base = in_ptr[v] + (t0 + 4 * u) * stride;
             if constexpr (kDma) {
                 const unsigned lds = (unsigned)(uintptr_t)(
@@ -403,7 +455,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
 #pragma unroll
                 for (int k = 0; k < kU; ++k) {
                     const int unit = kU * h + k, v = unit >> 3, u = unit & 7;
-                    if (nst == kTB || 4 * u + g < nst)
+                    if ((nst == kTB || 4 * u + g < nst) && !(zero_v && v == vV))
                         put4(&slot[b][v][u * 256], 4 * lane, InQuad<TIn>::f32(pre[k]));
                 }
             }
@@ -558,8 +610,8 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
         };
         auto ckpt_out = [&](int64_t blk) {
             const int64_t t = blk * kTB;
-            if (!ck_out || t % chunk != 0) return;
-            float *dst = ck_out + (bh * nck + t / chunk) * N * N;
+            if (!ck_out || (tb0 + t) % chunk != 0) return;
+            float *dst = ck_out + (bh * nck + (tb0 + t) / chunk) * N * N;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int row = 8 * h + 4 * k + g;
@@ -684,7 +736,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
 }
 
 template <typename TIn, bool kFused>
-hipError_t launch_fwdc_t(const FwdLaunch &a, hipStream_t stream)
+hipError_t launch_fwdc_t(const FwdLaunch &a, int mode, hipStream_t stream)
 {
     FwdcArgs<TIn> p;
     for (int i = 0; i < 6; ++i) p.in[i] = static_cast<const TIn *>(a.in[i]);
@@ -697,7 +749,13 @@ hipError_t launch_fwdc_t(const FwdLaunch &a, hipStream_t stream)
     p.H = a.H;
     p.chunk = a.chunk;
     p.nck = (int)((a.T + a.chunk - 1) / a.chunk);
-    hipLaunchKernelGGL((wkv7_fwdc_kernel<TIn, kFused>), dim3((unsigned)(a.B * a.H)), dim3(kThreads), 0,
+    p.mode = mode;
+    p.nseg = a.nseg;
+    p.nckseg = a.nckseg;
+    p.pbuf = a.pbuf;
+    const int64_t units = mode == 0 ? a.B * a.H
+                        : mode == 1 ? a.B * a.H * (2 * a.nseg - 3) : a.B * a.H * a.nseg;
+    hipLaunchKernelGGL((wkv7_fwdc_kernel<TIn, kFused>), dim3((unsigned)units), dim3(kThreads), 0,
                        stream, p);
     return hipGetLastError();
 }
@@ -709,11 +767,13 @@ bool forward_chunked_supported(const FwdLaunch &a)
     return a.N == 64 && a.chunk > 0 && a.chunk % kTB == 0;
 }
 
-hipError_t launch_forward_chunked(const FwdLaunch &a, hipStream_t stream)
+hipError_t launch_forward_chunked(const FwdLaunch &a, int mode, hipStream_t stream)
 {
     if (a.fused)
-        return a.dtype == 0 ? launch_fwdc_t<float, true>(a, stream) : launch_fwdc_t<uint16_t, true>(a, stream);
-    return a.dtype == 0 ? launch_fwdc_t<float, false>(a, stream) : launch_fwdc_t<uint16_t, false>(a, stream);
+        return a.dtype == 0 ? launch_fwdc_t<float, true>(a, mode, stream)
+                            : launch_fwdc_t<uint16_t, true>(a, mode, stream);
+    return a.dtype == 0 ? launch_fwdc_t<float, false>(a, mode, stream)
+                        : launch_fwdc_t<uint16_t, false>(a, mode, stream);
 }
 
 }  // namespace wkv7

@@ -20,6 +20,8 @@ struct FwdLaunch {
     int dtype;               // 0 f32, 1 bf16
     int chunk;               // checkpoint interval
     int fused;               // w, a, b slots hold omega, kk, gate (N = 64)
+    int nseg = 1, nckseg = 0;  // sequence split: segments of nckseg chunks
+    float *pbuf = nullptr;   // split: transition products, [B*H][nseg][64][64]
 };
 
 struct BwdLaunch {
@@ -36,6 +38,10 @@ struct BwdLaunch {
     int chunk;
     int algo;                // wkv7_algo
     int fused;               // as FwdLaunch; the chunk form only
+    int nseg = 1, nckseg = 0;  // sequence split (as the forward's)
+    const float *pbuf = nullptr;  // split: the forward's transition products
+    float *gbuf = nullptr;   // split: state gradients at segment starts
+    int *unit_flags = nullptr;  // split: chunk-form flags per (b, h, segment)
 };
 
 // The chunk forms address one (b) slice of a [B][T][H][64] tensor with
@@ -54,14 +60,21 @@ hipError_t launch_decode(const FwdLaunch &a, hipStream_t stream);
 // The forward for N = 64 on a scan plus matrix-core helper waves
 // (wkv7_fwdc.hip); it needs checkpoints on 32-step block starts.
 bool forward_chunked_supported(const FwdLaunch &a);
-hipError_t launch_forward_chunked(const FwdLaunch &a, hipStream_t stream);
+// mode 0: whole sequences; 1, 2: the two passes of a split sequence
+hipError_t launch_forward_chunked(const FwdLaunch &a, int mode, hipStream_t stream);
 // Reverse scan: the chunk form where it applies (and algo allows), then the
 // step-by-step scan for every head the chunk form flagged (or all heads).
 hipError_t launch_backward(const BwdLaunch &a, hipStream_t stream);
 // The chunk form (wkv7_bwdc.hip): N = 64, C = 64.  Writes flags[bh] = 1 for
 // heads whose decays it cannot take (their outputs are then undefined).
 bool chunked_backward_supported(const BwdLaunch &a);
-hipError_t launch_backward_chunked(const BwdLaunch &a, int *flags, hipStream_t stream);
+hipError_t launch_backward_chunked(const BwdLaunch &a, int *flags, int mode, hipStream_t stream);
+// Split sequences (wkv7_split.hip): carry-in states and state gradients
+// across segments, and the per-(b, h) fallback flags from the per-segment ones.
+hipError_t launch_compose_forward(const FwdLaunch &a, hipStream_t stream);
+hipError_t launch_compose_backward(const BwdLaunch &a, hipStream_t stream);
+hipError_t launch_flag_reduce(const int *unit_flags, int *flags, int64_t nbh, int nseg,
+                              hipStream_t stream);
 // dst[i] = src ? src[i] : 0 for i < n.
 hipError_t launch_fill(float *dst, const float *src, size_t n, hipStream_t stream);
 

@@ -138,6 +138,14 @@ def test_size_queries():
     assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == 9 * 16 * 16 * 4 + 65 * 16 * 4
     # no sub-checkpoints at C = 8; the flag ints round up to 256 bytes
     assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) == 256
+    # few, long sequences are split into segments: the record adds the
+    # segments' transition products, the workspace per-segment flags and
+    # the state gradients at segment starts (B=1, H=4, T=4096: 8 segments)
+    sh = _shape(B=1, T=4096, H=4, N=64)
+    states, tape = 4 * 64 * 4096 * 4, 4096 * 4 * 64 * 4
+    assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == states + tape + 4 * 8 * 4096 * 4
+    assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) == \
+        4 * 7 * 64 * 64 * 4 + 256 + 256 + 4 * 8 * 4096 * 4
     assert L.wkv7_checkpoint_bytes(ctypes.byref(_shape(N=48))) == 0
     assert L.wkv7_checkpoint_bytes(None) == 0
 

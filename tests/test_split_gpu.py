@@ -1,0 +1,98 @@
+"""Few, long sequences run in segments (the library splits a shape with at
+most 64 (b, h) pairs into up to 8 segments of at least 8 chunks, carrying
+states and state gradients between them): against the oracle, through the
+C ABI (MI355X only)."""
+import pytest
+import torch
+
+import oracle.fused as OF
+from linear_attention_rnn_wkv7_amd import api
+from linear_attention_rnn_wkv7_amd.synthetic import custom, make_inputs
+
+import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _check(out, ref, tau, label):
+    errs, bad = H.compare(out, ref, tau)
+    _say(f"{label}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    assert not bad, f"{label}: over {tau:g}*RMS: {bad} {errs}"
+
+
+# (B, T, H, dtype, s0, dsT): 2 segments; 8 segments of 8 chunks; 3 segments
+# with a ragged last chunk; bf16; a partial last 32-step block
+CASES = [
+    (1, 1024, 2, "f32", True, True),
+    (1, 4096, 4, "f32", False, True),
+    (2, 2000, 3, "f32", True, True),
+    (1, 1536, 2, "bf16", True, True),
+    (1, 1551, 1, "f32", True, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}_t{}_h{}_{}_s0{}_dsT{}".format(*c))
+def test_split_parity(case):
+    B, T, Hh, dt, s0, dsT = case
+    wl = custom(B, T, Hh, 64, dtype=dt, has_s0=s0, has_dsT=dsT, seed=700 + T)
+    _say(f"case split {wl.name}")
+    inp = make_inputs(wl, device="cuda")
+    out = H.gpu_run(inp)
+    torch.cuda.synchronize()
+    _check(out, H.oracle_run(inp), H.TAU[inp["r"].dtype], wl.name)
+
+
+def test_split_recompute_and_scan():
+    """The backward recomputing the (split) forward into its workspace gives
+    the same bits as the handed-over record; the step scan (no split in the
+    backward) reads the same record."""
+    wl = custom(1, 2048, 3, 64, has_s0=True, has_dsT=True, seed=31)
+    inp = make_inputs(wl, device="cuda")
+    a = H.gpu_run(inp, ckpt_handoff=True)
+    b = H.gpu_run(inp, ckpt_handoff=False)
+    for n in H.GRADS + ("ds0",):
+        assert torch.equal(a[n], b[n]), n
+    s = H.gpu_run(inp, algo="scan")
+    ref = H.oracle_run(inp)
+    _check(s, ref, 2e-4, "scan on the split record")
+
+
+def test_split_fused():
+    wl = custom(1, 2048, 2, 64, has_s0=True, has_dsT=True, seed=41)
+    _say(f"case split fused {wl.name}")
+    inp = make_inputs(wl, device="cuda", fused=True)
+    y, sT, ck = api.wkv7_forward(*(inp[n] for n in H.IN), inp["s0"], want_ckpt=True, fused=True)
+    g = api.wkv7_backward(*(inp[n] for n in H.IN), inp["dy"], inp["s0"], inp["dsT"], ck, fused=True)
+    torch.cuda.synchronize()
+    out = dict(g)
+    out["y"], out["sT"] = y, sT
+    sl = {n: H.to64(inp[n]) for n in H.IN + ("dy",)}
+    ry, rs = OF.forward(*(sl[n] for n in H.IN), s0=H.to64(inp["s0"]))
+    ref = OF.backward(*(sl[n] for n in H.IN), sl["dy"], s0=H.to64(inp["s0"]), dsT=H.to64(inp["dsT"]))
+    ref["y"], ref["sT"] = ry, rs
+    _check(out, ref, 2e-4, "split fused")
+
+
+def test_split_falls_back_per_head():
+    """A head with a decay out of the chunk form's range in any segment is
+    redone whole by the step scan (bitwise equal to it); the others are not."""
+    wl = custom(2, 1280, 3, 64, has_s0=True, has_dsT=True, seed=23)
+    _say(f"case split fallback {wl.name}")
+    inp = make_inputs(wl, device="cuda")
+    w = inp["w"]
+    w[1, 1000, 2, 7] = 0.0         # a decay of 0 in the second segment
+    w[0, 100:120, 1, :] = 0.02     # decays below 1/16 in the first segment
+    flagged = [(1, 2), (0, 1)]
+    a = H.gpu_run(inp)
+    s = H.gpu_run(inp, algo="scan")
+    torch.cuda.synchronize()
+    _check(a, H.oracle_run(inp), 2e-4, "split fallback")
+    for b in range(wl.B):
+        for h in range(wl.H):
+            same = all(torch.equal(a[n][b, :, h], s[n][b, :, h]) for n in H.GRADS) and \
+                torch.equal(a["ds0"][b, h], s["ds0"][b, h])
+            assert same == ((b, h) in flagged), (b, h, same)
