@@ -121,13 +121,19 @@ enum {
 };
 
 /* Bytes of the checkpoint record for `shape`:
- * roundup(B*H*ceil(T/C)*N*N*4, 256) + B*T*H*N*4; 0 when the shape is invalid. */
+ * roundup(B*H*ceil(T/C)*N*N*4, 256) + B*T*H*N*4; 0 when the shape is invalid.
+ * Shapes of few, long sequences run split into segments (N = 64, C = 64,
+ * T*H*64*4 < 2^31, B*H <= 64, at least 16 chunks; the count, up to 8, and
+ * the segment length follow from the shape): their record rounds the sa
+ * part up to 256 bytes and adds the segments' transition products,
+ * B*H*nseg*N*N*4 bytes.  Only a wkv7_forward with a record runs split. */
 size_t wkv7_checkpoint_bytes(const wkv7_shape *shape);
 
 /* Bytes of device workspace wkv7_backward needs: the per-(b,h) state
- * sub-checkpoints of one chunk and one int per (b,h), plus room for the
- * checkpoint record itself when `ckpt_provided` is 0.  0 when the shape is
- * invalid or empty. */
+ * sub-checkpoints of one chunk and one int per (b,h) (for a split shape
+ * also one int and one N x N fp32 state gradient per (b,h) and segment),
+ * plus room for the checkpoint record itself when `ckpt_provided` is 0.
+ * 0 when the shape is invalid or empty. */
 size_t wkv7_backward_workspace_bytes(const wkv7_shape *shape, int ckpt_provided);
 
 /* Forward scan (rx_wkv7_forward_seq on the Foundry rx_pretrain.c page).
