@@ -375,6 +375,69 @@ def pin_fused_torch_autograd(rng, lib=None, B=1, T=5, H=2, N=4):
                for n, gn in list(zip(NAMES_IN, NAMES_GRAD)) + [("s0", "ds0")])
 
 
+# ------------------------------------------- epilogue (oracle.epilogue)
+def rand_epilogue(rng, B, T, H, N):
+    shp = (B, T, H, N)
+    d = {n: rng.standard_normal(shp) for n in ("y", "r", "k", "v", "dz")}
+    d["y"] = 3.0 * d["y"] + 0.5
+    d["g"] = 1.0 / (1.0 + np.exp(-rng.standard_normal(shp)))
+    for n in ("ln_w", "ln_b", "r_k"):
+        d[n] = rng.standard_normal((H, N))
+    return d
+
+
+EPI_IN = ("y", "r", "k", "v", "g", "ln_w", "ln_b", "r_k")
+EPI_GRAD = {"y": "dy", "r": "dr", "k": "dk", "v": "dv", "g": "dg", "ln_w": "dln_w",
+            "ln_b": "dln_b", "r_k": "dr_k"}
+
+
+def pin_epilogue_finite_differences(rng, lib=None, B=1, T=3, H=2, N=5, h=1e-6):
+    """Central differences of L = sum dz . z for every input element and
+    parameter of the group norm + bonus + gate epilogue."""
+    import oracle.epilogue as E
+    d = rand_epilogue(rng, B, T, H, N)
+    g = E.backward(d["dz"], *(d[n] for n in EPI_IN))
+
+    def L():
+        return float(np.sum(d["dz"] * E.forward(*(d[n] for n in EPI_IN))))
+    worst = 0.0
+    for n in EPI_IN:
+        fd = np.zeros_like(d[n])
+        for idx in np.ndindex(d[n].shape):
+            keep = d[n][idx]
+            d[n][idx] = keep + h
+            lp = L()
+            d[n][idx] = keep - h
+            lm = L()
+            d[n][idx] = keep
+            fd[idx] = (lp - lm) / (2 * h)
+        worst = max(worst, rel(g[EPI_GRAD[n]], fd))
+    return worst
+
+
+def pin_epilogue_torch(rng, lib=None, B=2, T=3, H=2, N=8):
+    """torch's own group norm (F.group_norm, one group per head) and autograd
+    against the forward and every gradient."""
+    import torch
+    import torch.nn.functional as F
+
+    import oracle.epilogue as E
+    d = rand_epilogue(rng, B, T, H, N)
+    z = E.forward(*(d[n] for n in EPI_IN))
+    g = E.backward(d["dz"], *(d[n] for n in EPI_IN))
+    tv = {n: torch.tensor(d[n], dtype=torch.float64, requires_grad=True) for n in EPI_IN}
+    yy = tv["y"].reshape(B * T, H * N)
+    yn = F.group_norm(yy, H, tv["ln_w"].reshape(-1), tv["ln_b"].reshape(-1), eps=E.EPS)
+    yn = yn.reshape(B, T, H, N)
+    s = (tv["r"] * tv["k"] * tv["r_k"]).sum(-1, keepdim=True)
+    zt = (yn + s * tv["v"]) * tv["g"]
+    (torch.tensor(d["dz"]) * zt).sum().backward()
+    errs = [rel(z, zt.detach().numpy())]
+    for n in EPI_IN:
+        errs.append(rel(g[EPI_GRAD[n]], tv[n].grad.numpy()))
+    return max(errs)
+
+
 ALL_PINS = {
     "golden_n1": (lambda rng, lib: pin_golden("hand_n1_t2.txt", lib), 1e-15),
     "golden_n2": (lambda rng, lib: pin_golden("hand_n2_t1.txt", lib), 1e-15),
@@ -389,4 +452,6 @@ ALL_PINS = {
     "exact_rational": (pin_exact_rational, 1e-13),
     "fused_finite_differences": (pin_fused_finite_differences, 1e-7),
     "fused_torch_autograd": (pin_fused_torch_autograd, 1e-12),
+    "epilogue_finite_differences": (pin_epilogue_finite_differences, 1e-7),
+    "epilogue_torch_group_norm": (pin_epilogue_torch, 1e-12),
 }
