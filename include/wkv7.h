@@ -177,6 +177,37 @@ int wkv7_backward(const wkv7_shape *shape,
                   hipStream_t stream);
 
 /* Static text for a status code. */
+/* The time-mix epilogue after the scan, N = 64 (Foundry page
+ * "rwkvx/rx_pretrain.c": gn_forward, the bonus term and the gate g applied
+ * to the scan's output in rx_timemix_forward_seq, and the per-token
+ * post-processing backward of its backward), per (b, t, h) over the head's
+ * 64 entries:
+ *   z = ((y - mean) * rstd * ln_w + ln_b + s * v) * g,
+ *   rstd = 1 / sqrt(var + 64e-5),  s = sum_j r_j * k_j * r_k[j].
+ * One pass over the tensors each way.  The output projection that follows on
+ * the page is not part of it.
+ *   y, dz      : fp32 [B][T][H][64]; r, k, v, g: [B][T][H][64], dtype per
+ *                shape->dtype (the scan's r, k, v and the gate).
+ *   ln_w, ln_b, r_k : fp32 [H][64] per-channel parameters.
+ *   z          : fp32 [B][T][H][64] output.
+ * The backward returns dy (the scan's output gradient, to hand to
+ * wkv7_backward), dg, the bonus term's shares of dr, dk, dv (to add to the
+ * scan's), all fp32 [B][T][H][64], and dln_w, dln_b, dr_k (fp32 [H][64],
+ * summed over b and t in a fixed order: reproducible bit for bit), with a
+ * workspace of wkv7_epilogue_workspace_bytes(shape) bytes, 256-byte
+ * aligned.  The shape's chunk, algo and flags fields must be valid and are
+ * otherwise unused.  N != 64 is WKV7_ERR_UNSUPPORTED; no output may overlap
+ * an input; B*T == 0 gives zero parameter gradients. */
+size_t wkv7_epilogue_workspace_bytes(const wkv7_shape *shape);
+int wkv7_epilogue_forward(const wkv7_shape *shape, const float *y, const void *r, const void *k,
+                          const void *v, const void *g, const float *ln_w, const float *ln_b,
+                          const float *r_k, float *z, hipStream_t stream);
+int wkv7_epilogue_backward(const wkv7_shape *shape, const float *dz, const float *y, const void *r,
+                           const void *k, const void *v, const void *g, const float *ln_w,
+                           const float *ln_b, const float *r_k, float *dy, float *dg, float *dr,
+                           float *dk, float *dv, float *dln_w, float *dln_b, float *dr_k,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 const char *wkv7_status_string(int status);
 
 /* ABI version (major * 100 + minor). */

@@ -15,7 +15,8 @@ WKV7_OK, WKV7_ERR_INVALID, WKV7_ERR_UNSUPPORTED, WKV7_ERR_WORKSPACE, WKV7_ERR_HI
 
 # Every function the C header declares, for the symbol-export test.
 EXPORTS = ("wkv7_checkpoint_bytes", "wkv7_backward_workspace_bytes", "wkv7_forward",
-           "wkv7_backward", "wkv7_status_string", "wkv7_abi_version")
+           "wkv7_backward", "wkv7_epilogue_workspace_bytes", "wkv7_epilogue_forward",
+           "wkv7_epilogue_backward", "wkv7_status_string", "wkv7_abi_version")
 
 
 WKV7_FUSED_INPUTS = 1   # wkv7_shape.flags bit
@@ -55,6 +56,12 @@ def lib():
     L.wkv7_forward.restype = i32
     L.wkv7_backward.argtypes = [sp] + [vp] * 17 + [vp, sz, vp]
     L.wkv7_backward.restype = i32
+    L.wkv7_epilogue_workspace_bytes.argtypes = [sp]
+    L.wkv7_epilogue_workspace_bytes.restype = sz
+    L.wkv7_epilogue_forward.argtypes = [sp] + [vp] * 9 + [vp]
+    L.wkv7_epilogue_forward.restype = i32
+    L.wkv7_epilogue_backward.argtypes = [sp] + [vp] * 17 + [vp, sz, vp]
+    L.wkv7_epilogue_backward.restype = i32
     L.wkv7_status_string.argtypes = [i32]
     L.wkv7_status_string.restype = ctypes.c_char_p
     L.wkv7_abi_version.argtypes = []

@@ -126,3 +126,49 @@ def wkv7_backward(r, w, k, v, a, b, dy, s0=None, dsT=None, ckpt=None, *, chunk=6
         _ptr(workspace), ws_bytes, _stream(stream))
     _lib.check("wkv7_backward", rc)
     return grads
+
+
+def _check_f32(name, t, shape):
+    if t.shape != shape or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous fp32 device tensor {list(shape)}")
+
+
+def wkv7_epilogue_forward(y, r, k, v, g, ln_w, ln_b, r_k, *, stream=None, out=None):
+    """Group norm, bonus and gate after the scan (wkv7_epilogue_forward):
+    z = ((y - mean) rstd ln_w + ln_b + (sum r k r_k) v) g per (b, t, h)."""
+    (B, T, H, N), dt = _check_vecs("rkvg", (r, k, v, g))
+    _check_f32("y", y, (B, T, H, N))
+    for n, p in (("ln_w", ln_w), ("ln_b", ln_b), ("r_k", r_k)):
+        _check_f32(n, p, (H, N))
+    z = out if out is not None else torch.empty((B, T, H, N), device=y.device, dtype=torch.float32)
+    sh = make_shape(B, T, H, N, dt)
+    rc = _lib.lib().wkv7_epilogue_forward(ctypes.byref(sh), *map(_ptr, (y, r, k, v, g, ln_w, ln_b, r_k, z)),
+                                          _stream(stream))
+    _lib.check("wkv7_epilogue_forward", rc)
+    return z
+
+
+def wkv7_epilogue_backward(dz, y, r, k, v, g, ln_w, ln_b, r_k, *, workspace=None, stream=None):
+    """The epilogue's backward: dict(dy, dg, dr, dk, dv, dln_w, dln_b, dr_k);
+    dr, dk, dv are the bonus term's shares (added to the scan's by the caller)."""
+    (B, T, H, N), dt = _check_vecs("rkvg", (r, k, v, g))
+    _check_f32("y", y, (B, T, H, N))
+    _check_f32("dz", dz, (B, T, H, N))
+    for n, p in (("ln_w", ln_w), ("ln_b", ln_b), ("r_k", r_k)):
+        _check_f32(n, p, (H, N))
+    dev = y.device
+    out = {n: torch.empty((B, T, H, N), device=dev, dtype=torch.float32)
+           for n in ("dy", "dg", "dr", "dk", "dv")}
+    for n in ("dln_w", "dln_b", "dr_k"):
+        out[n] = torch.empty((H, N), device=dev, dtype=torch.float32)
+    sh = make_shape(B, T, H, N, dt)
+    need = _lib.lib().wkv7_epilogue_workspace_bytes(ctypes.byref(sh))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _lib.lib().wkv7_epilogue_backward(
+        ctypes.byref(sh), *map(_ptr, (dz, y, r, k, v, g, ln_w, ln_b, r_k)),
+        *map(_ptr, (out[n] for n in ("dy", "dg", "dr", "dk", "dv", "dln_w", "dln_b", "dr_k"))),
+        _ptr(workspace), ws_bytes, _stream(stream))
+    _lib.check("wkv7_epilogue_backward", rc)
+    return out

@@ -318,6 +318,95 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
     return hip_status(wkv7::launch_backward(L, stream));
 }
 
+size_t wkv7_epilogue_workspace_bytes(const wkv7_shape *shape)
+{
+    Dims d;
+    if (check_shape(shape, &d) != WKV7_OK || d.N != 64 || d.B * d.T * d.H == 0) return 0;
+    return round_up((size_t)d.H * wkv7::epilogue_chunks(d.B * d.T, d.H) * 3 * 64 * sizeof(float));
+}
+
+int wkv7_epilogue_forward(const wkv7_shape *shape, const float *y, const void *r, const void *k,
+                          const void *v, const void *g, const float *ln_w, const float *ln_b,
+                          const float *r_k, float *z, hipStream_t stream)
+{
+    Dims d;
+    int rc = check_shape(shape, &d);
+    if (rc != WKV7_OK) return rc;
+    if (d.N != 64) return WKV7_ERR_UNSUPPORTED;
+    if (d.B * d.T * d.H == 0) return WKV7_OK;
+    for (const void *p : {(const void *)y, r, k, v, g, (const void *)ln_w, (const void *)ln_b,
+                          (const void *)r_k, (const void *)z})
+        if (!p || !aligned(p)) return WKV7_ERR_INVALID;
+    wkv7::EpiLaunch L;
+    L.y = y;
+    L.r = r;
+    L.k = k;
+    L.v = v;
+    L.g = g;
+    L.ln_w = ln_w;
+    L.ln_b = ln_b;
+    L.r_k = r_k;
+    L.z = z;
+    L.BT = d.B * d.T;
+    L.H = d.H;
+    L.dtype = d.dtype;
+    return hip_status(wkv7::launch_epilogue_forward(L, stream));
+}
+
+int wkv7_epilogue_backward(const wkv7_shape *shape, const float *dz, const float *y, const void *r,
+                           const void *k, const void *v, const void *g, const float *ln_w,
+                           const float *ln_b, const float *r_k, float *dy, float *dg, float *dr,
+                           float *dk, float *dv, float *dln_w, float *dln_b, float *dr_k,
+                           void *workspace, size_t workspace_bytes_given, hipStream_t stream)
+{
+    Dims d;
+    int rc = check_shape(shape, &d);
+    if (rc != WKV7_OK) return rc;
+    if (d.N != 64) return WKV7_ERR_UNSUPPORTED;
+    if (d.H == 0) return WKV7_OK;
+    for (const void *p : {(const void *)ln_w, (const void *)ln_b, (const void *)r_k, (const void *)dln_w,
+                          (const void *)dln_b, (const void *)dr_k})
+        if (!p || !aligned(p)) return WKV7_ERR_INVALID;
+    if (d.B * d.T == 0) {   // no rows: the parameter gradients are zero
+        for (float *p : {dln_w, dln_b, dr_k}) {
+            rc = hip_status(wkv7::launch_fill(p, nullptr, (size_t)d.H * 64, stream));
+            if (rc != WKV7_OK) return rc;
+        }
+        return WKV7_OK;
+    }
+    for (const void *p : {(const void *)dz, (const void *)y, r, k, v, g, (const void *)dy,
+                          (const void *)dg, (const void *)dr, (const void *)dk, (const void *)dv})
+        if (!p || !aligned(p)) return WKV7_ERR_INVALID;
+    const int nchunk = wkv7::epilogue_chunks(d.B * d.T, d.H);
+    const size_t need = round_up((size_t)d.H * nchunk * 3 * 64 * sizeof(float));
+    if (!workspace || workspace_bytes_given < need || ((uintptr_t)workspace % kAlign) != 0)
+        return WKV7_ERR_WORKSPACE;
+    wkv7::EpiLaunch L;
+    L.y = y;
+    L.dz = dz;
+    L.r = r;
+    L.k = k;
+    L.v = v;
+    L.g = g;
+    L.ln_w = ln_w;
+    L.ln_b = ln_b;
+    L.r_k = r_k;
+    L.dy = dy;
+    L.dg = dg;
+    L.dr = dr;
+    L.dk = dk;
+    L.dv = dv;
+    L.dln_w = dln_w;
+    L.dln_b = dln_b;
+    L.dr_k = dr_k;
+    L.part = static_cast<float *>(workspace);
+    L.BT = d.B * d.T;
+    L.H = d.H;
+    L.dtype = d.dtype;
+    L.nchunk = nchunk;
+    return hip_status(wkv7::launch_epilogue_backward(L, stream));
+}
+
 const char *wkv7_status_string(int status)
 {
     switch (status) {
@@ -332,7 +421,7 @@ const char *wkv7_status_string(int status)
 
 int wkv7_abi_version(void)
 {
-    return 103;
+    return 104;
 }
 
 }  // extern "C"

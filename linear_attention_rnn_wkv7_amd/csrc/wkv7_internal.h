@@ -75,6 +75,23 @@ hipError_t launch_compose_forward(const FwdLaunch &a, hipStream_t stream);
 hipError_t launch_compose_backward(const BwdLaunch &a, hipStream_t stream);
 hipError_t launch_flag_reduce(const int *unit_flags, int *flags, int64_t nbh, int nseg,
                               hipStream_t stream);
+// The time-mix epilogue (wkv7_epilogue.hip): group norm, bonus and gate
+// after the scan, N = 64; rows are the B*T*H (b, t, h) of [B][T][H][64].
+struct EpiLaunch {
+    const float *y = nullptr, *dz = nullptr;
+    const void *r = nullptr, *k = nullptr, *v = nullptr, *g = nullptr;   // dtype
+    const float *ln_w = nullptr, *ln_b = nullptr, *r_k = nullptr;        // [H][64]
+    float *z = nullptr;
+    float *dy = nullptr, *dg = nullptr, *dr = nullptr, *dk = nullptr, *dv = nullptr;
+    float *dln_w = nullptr, *dln_b = nullptr, *dr_k = nullptr;
+    float *part = nullptr;   // backward: [H][nchunk][3][64] partial sums
+    int64_t BT = 0, H = 0;
+    int dtype = 0, nchunk = 1;
+};
+// Backward workgroups per head (each a range of (b, t)).
+int epilogue_chunks(int64_t BT, int64_t H);
+hipError_t launch_epilogue_forward(const EpiLaunch &a, hipStream_t stream);
+hipError_t launch_epilogue_backward(const EpiLaunch &a, hipStream_t stream);
 // dst[i] = src ? src[i] : 0 for i < n.
 hipError_t launch_fill(float *dst, const float *src, size_t n, hipStream_t stream);
 

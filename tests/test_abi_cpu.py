@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.wkv7_abi_version() == 103
+    assert L.wkv7_abi_version() == 104
 
 
 def _shape(B=2, T=10, H=3, N=64, dtype=0, chunk=64, algo=0, flags=0):
@@ -148,6 +148,41 @@ def test_size_queries():
         4 * 7 * 64 * 64 * 4 + 256 + 256 + 4 * 8 * 4096 * 4
     assert L.wkv7_checkpoint_bytes(ctypes.byref(_shape(N=48))) == 0
     assert L.wkv7_checkpoint_bytes(None) == 0
+
+
+def test_epilogue_validation():
+    L = _lib.lib()
+    f = ctypes.c_void_p(FAKE)
+
+    def fwd(sh, over=None):
+        p = [f] * 9
+        for i, val in (over or {}).items():
+            p[i] = val
+        return L.wkv7_epilogue_forward(ctypes.byref(sh), *p, None)
+
+    def bwd(sh, ws=None, ws_bytes=0, null_at=None):
+        p = [f] * 17
+        if null_at is not None:
+            p[null_at] = None
+        return L.wkv7_epilogue_backward(ctypes.byref(sh), *p, ws, ws_bytes, None)
+
+    sh = _shape(B=2, T=10, H=3, N=64)
+    assert fwd(_shape(N=16)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert fwd(_shape(B=-1)) == _lib.WKV7_ERR_INVALID
+    for i in range(9):
+        assert fwd(sh, {i: None}) == _lib.WKV7_ERR_INVALID, i
+        assert fwd(sh, {i: ctypes.c_void_p(FAKE + 4)}) == _lib.WKV7_ERR_INVALID, i
+    assert fwd(_shape(B=0)) == _lib.WKV7_OK
+    assert bwd(_shape(N=16)) == _lib.WKV7_ERR_UNSUPPORTED
+    for i in range(17):
+        assert bwd(sh, null_at=i) == _lib.WKV7_ERR_INVALID, i
+    need = L.wkv7_epilogue_workspace_bytes(ctypes.byref(sh))
+    assert need > 0 and need % 256 == 0
+    assert bwd(sh) == _lib.WKV7_ERR_WORKSPACE
+    assert bwd(sh, f, need - 1) == _lib.WKV7_ERR_WORKSPACE
+    assert bwd(sh, ctypes.c_void_p(FAKE + 16), need) == _lib.WKV7_ERR_WORKSPACE
+    assert bwd(_shape(H=0)) == _lib.WKV7_OK
+    assert L.wkv7_epilogue_workspace_bytes(ctypes.byref(_shape(N=16))) == 0
 
 
 def test_status_strings():
