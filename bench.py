@@ -22,6 +22,10 @@ d omega, d kk, d gate) and adds ``unfused_pipeline_ms``: the same result
 from the plain kernels with torch forming w, a, b before and chaining the
 gradients after, the element-wise HBM passes the fused form saves.
 
+``--epilogue`` times the time-mix epilogue after the scan (group norm,
+bonus, gate; wkv7_epilogue_forward and _backward) on the workload's shape,
+an HBM-bound pass each way, against the 8 TB/s roofline.
+
 A workload with T = 1 (``--workload decode_b256_t1_h32_n64``) times the
 decode step of batched inference instead: one forward step of every (b, h)
 from its carry-in state, bound by HBM bandwidth (each (b, h) reads and
@@ -187,6 +191,90 @@ def unfused_pipeline_ms(api, inp, names, C, ck, ws, y, sT, grads, stream, args):
     return e0.elapsed_time(e1) / args.steps
 
 
+EPILOGUE_METRIC = "WKV7 epilogue (group norm, bonus, gate) fwd+bwd tokens/sec at 1 GPU; % of HBM roofline"
+
+
+def epilogue_bench(args, wl):
+    import ctypes
+
+    import torch
+
+    import oracle.epilogue as OE
+    from linear_attention_rnn_wkv7_amd import api
+    from linear_attention_rnn_wkv7_amd.synthetic import make_inputs
+
+    inp = make_inputs(wl, device="cuda")
+    B, T, H, N = wl.B, wl.T, wl.H, wl.N
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed + 1)
+    shp = (B, T, H, N)
+    y = 4.0 * torch.randn(shp, generator=gen, device="cuda")
+    g = torch.sigmoid(torch.randn(shp, generator=gen, device="cuda")).to(inp["r"].dtype)
+    dz = torch.randn(shp, generator=gen, device="cuda")
+    par = [1.0 + 0.1 * torch.randn((H, N), generator=gen, device="cuda"),
+           0.1 * torch.randn((H, N), generator=gen, device="cuda"),
+           0.5 * torch.randn((H, N), generator=gen, device="cuda")]
+    args_ = (y, inp["r"], inp["k"], inp["v"], g, *par)
+    z = torch.empty(shp, device="cuda", dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+    sh = api.make_shape(B, T, H, N, inp["r"].dtype)
+    ws = torch.empty(max(1, api._lib.lib().wkv7_epilogue_workspace_bytes(ctypes.byref(sh))),
+                     device="cuda", dtype=torch.uint8)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    f_ms = timed(lambda: api.wkv7_epilogue_forward(*args_, out=z, stream=stream))
+    b_ms = timed(lambda: api.wkv7_epilogue_backward(dz, *args_, workspace=ws, stream=stream))
+    eb = 4 if wl.dtype == "f32" else 2
+    rows_el = B * T * H * N
+    f_bytes = rows_el * (4 + 4 * eb + 4)          # y, r, k, v, g in; z out
+    b_bytes = rows_el * (8 + 4 * eb + 20)         # dz, y, r, k, v, g in; dy, dg, dr, dk, dv out
+    ms = f_ms + b_ms
+    achieved = (f_bytes + b_bytes) / (ms * 1e-3)
+    rec = {
+        "metric": EPILOGUE_METRIC, "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "N": N, "input_dtype": wl.dtype,
+                   "epilogue": True},
+        "roofline": {"kernel": "epi_fwd_kernel + epi_bwd_kernel", "bound": "hbm",
+                     "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM, "traffic": None},
+        "fwd_ms": f_ms, "bwd_ms": b_ms,
+        "fwd_gbps": f_bytes / (f_ms * 1e-3) / 1e9, "bwd_gbps": b_bytes / (b_ms * 1e-3) / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on a bounded sample of (b, t) rows (all heads)
+        nb = max(1, min(B, 1))
+        nt = min(T, 512)
+        h = {n: x[:nb, :nt].detach().cpu().double().numpy() for n, x in
+             (("y", y), ("r", inp["r"]), ("k", inp["k"]), ("v", inp["v"]), ("g", g), ("dz", dz))}
+        hp = [p.cpu().double().numpy() for p in par]
+        t0, reps = time.perf_counter(), 0
+        while True:
+            OE.forward(h["y"], h["r"], h["k"], h["v"], h["g"], *hp)
+            OE.backward(h["dz"], h["y"], h["r"], h["k"], h["v"], h["g"], *hp)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_budget, 10.0):
+                break
+        rec["cpu_baseline"] = {"value": reps * nb * nt / el, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{reps} x ({nb} x {nt} tokens, all {H} heads), fp64 numpy "
+                                         f"fwd+bwd in {el:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs,
     or None when absent or taken on a different kernel source."""
@@ -268,6 +356,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused", action="store_true",
                     help="fused time-mix inputs (WKV7_FUSED_INPUTS)")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="time the epilogue (group norm, bonus, gate) instead of the scan")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run a plain device copy of this many bytes (the "
                          "reference point for the HBM traffic counters)")
@@ -285,6 +375,8 @@ def main():
     from linear_attention_rnn_wkv7_amd.synthetic import WORKLOADS, make_inputs
 
     wl = WORKLOADS[args.workload]
+    if args.epilogue:
+        return epilogue_bench(args, wl)
     if wl.T == 1:
         return decode_bench(args, wl)
     names = ("r", "w", "k", "v", "a", "b")

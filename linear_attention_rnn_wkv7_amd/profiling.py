@@ -45,7 +45,7 @@ def kernel_sha(kernel=None):
 
 
 def _short(name):
-    m = re.search(r"(wkv7_\w+_kernel|fill_kernel)", name)
+    m = re.search(r"(wkv7_\w+_kernel|epi_\w+_kernel|compose_\w+_kernel|flag_reduce_kernel|fill_kernel)", name)
     if m:
         return m.group(1)
     return name[:60]
