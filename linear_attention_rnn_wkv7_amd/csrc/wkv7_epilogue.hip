@@ -95,6 +95,7 @@ __global__ void __launch_bounds__(256) epi_bwd_kernel(EpiArgs<TIn> p)
     const int64_t bt0 = (int64_t)c * p.chunk_rows;
     int64_t bt1 = bt0 + p.chunk_rows;
     if (bt1 > p.bt) bt1 = p.bt;
+#pragma unroll 2
     for (int64_t bt = bt0 + grp; bt < bt1; bt += 16) {
         const int64_t o = (bt * p.H + h) * N + 4 * l;
         float rstd;
@@ -145,6 +146,7 @@ __global__ void epi_reduce_kernel(const float *part, float *dlw, float *dlb, flo
     const int kind = (int)(i / (H * N));
     const int64_t hj = i % (H * N), h = hj / N, j = hj % N;
     float acc = 0.f;
+#pragma unroll 16
     for (int c = 0; c < nchunk; ++c) acc += part[((h * nchunk + c) * 3 + kind) * N + j];
     (kind == 0 ? dlw : kind == 1 ? dlb : drk)[hj] = acc;
 }
