@@ -126,7 +126,9 @@ enum {
  * T*H*64*4 < 2^31, B*H <= 64, at least 16 chunks; the count, up to 8, and
  * the segment length follow from the shape): their record rounds the sa
  * part up to 256 bytes and adds the segments' transition products,
- * B*H*nseg*N*N*4 bytes.  Only a wkv7_forward with a record runs split. */
+ * B*H*nseg*N*N*4 bytes.  A wkv7_forward with no record runs split when it
+ * writes y, keeping the carries between segments in y's own rows until
+ * the segments overwrite them with their outputs. */
 size_t wkv7_checkpoint_bytes(const wkv7_shape *shape);
 
 /* Bytes of device workspace wkv7_backward needs: the per-(b,h) state

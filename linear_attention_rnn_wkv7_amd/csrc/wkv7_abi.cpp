@@ -221,6 +221,15 @@ int wkv7_forward(const wkv7_shape *shape, const void *r, const void *w, const vo
         L.nseg = d.nseg;
         L.nckseg = d.nckseg;
         L.pbuf = pbuf_of(ckpt, d);
+    } else if (!ckpt && y && d.nseg > 1) {
+        // no record: the carries go into the segments' own rows of y (a
+        // state takes N steps of a (b, h), a carry and a transition product
+        // 2N; segments but the last have at least 8 chunks, and the last at
+        // least 2 under plan_split, so this check always passes)
+        if (d.T - (int64_t)(d.nseg - 1) * d.nckseg * d.C >= d.N) {
+            L.nseg = d.nseg;
+            L.nckseg = d.nckseg;
+        }
     }
     return hip_status(wkv7::launch_forward(L, stream));
 }

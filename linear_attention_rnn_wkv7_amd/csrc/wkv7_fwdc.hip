@@ -109,8 +109,13 @@ struct FwdcArgs {
     // with v = 0 from the identity, giving the segment's transition product
     // P_s (into pbuf), and writes nothing else; mode 2 runs every segment
     // from its carry-in state (the checkpoint at its start) with all outputs.
+    // Without a checkpoint record the carries live in y instead, in rows of
+    // (b, h) that segment s overwrites itself: steps 0 .. 63 of segment s
+    // hold its carry-in state (Q_{s-1}, then S_in(s)), steps 64 .. 127 its
+    // P_s; every segment but the last spans at least 128 steps and the last
+    // at least 64.  A unit reads its carry-in state before any y store.
     int mode, nseg, nckseg;
-    float *pbuf;   // [B*H][nseg][64][64]
+    float *pbuf;   // [B*H][nseg][64][64]; null when the carries live in y
 };
 
 template <typename TIn, bool kFused>
@@ -136,9 +141,15 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
     int64_t bh = blockIdx.x, tb0 = 0, T = p.T;
     const float *s0u = p.s0 ? p.s0 + bh * N * N : nullptr;
     float *sTu = p.sT ? p.sT + bh * N * N : nullptr;
+    int64_t s0ld = N, sTld = N;   // row strides of the two states
     bool s0_eye = false, zero_v = false, outs = true;
     if (p.mode != 0) {
         const int64_t Tseg = (int64_t)p.nckseg * p.chunk;
+        const bool in_y = p.ckpt == nullptr;   // the carries live in y
+        // row `row` of segment s's part of the sequence of (b, h) in y
+        auto yrow = [&](int s, int row) {
+            return p.y + ((bh / H) * p.T * H + bh % H) * N + ((int64_t)s * Tseg + row) * H * N;
+        };
         int seg;
         if (p.mode == 1) {
             const int per = 2 * p.nseg - 3, k = (int)((int64_t)blockIdx.x % per);
@@ -147,18 +158,25 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
             if (k < p.nseg - 1) {   // Q_s
                 seg = k;
                 s0u = seg == 0 && p.s0 ? p.s0 + bh * N * N : nullptr;
-                sTu = p.ckpt + (bh * p.nck + (int64_t)(seg + 1) * p.nckseg) * N * N;
+                sTu = in_y ? yrow(seg + 1, 0) : p.ckpt + (bh * p.nck + (int64_t)(seg + 1) * p.nckseg) * N * N;
             } else {                // P_s
                 seg = k - (p.nseg - 1) + 1;
                 s0u = nullptr;
                 s0_eye = zero_v = true;
-                sTu = p.pbuf + (bh * p.nseg + seg) * N * N;
+                sTu = in_y ? yrow(seg, N) : p.pbuf + (bh * p.nseg + seg) * N * N;
             }
+            if (in_y) sTld = H * N;
         } else {
             bh = (int64_t)blockIdx.x / p.nseg;
             seg = (int)((int64_t)blockIdx.x % p.nseg);
-            s0u = seg == 0 ? (p.s0 ? p.s0 + bh * N * N : nullptr)
-                           : p.ckpt + (bh * p.nck + (int64_t)seg * p.nckseg) * N * N;
+            if (seg == 0) {
+                s0u = p.s0 ? p.s0 + bh * N * N : nullptr;
+            } else if (in_y) {
+                s0u = yrow(seg, 0);
+                s0ld = H * N;
+            } else {
+                s0u = p.ckpt + (bh * p.nck + (int64_t)seg * p.nckseg) * N * N;
+            }
             sTu = seg == p.nseg - 1 && p.sT ? p.sT + bh * N * N : nullptr;
         }
         tb0 = seg * Tseg;
@@ -195,12 +213,12 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
 #pragma unroll
                 for (int c = 0; c < CC; ++c) S[e][c] = row0 + e == col0 + c ? 1.f : 0.f;
         } else if (s0u) {
-            const float *src = s0u + (int64_t)row0 * N + col0;
+            const float *src = s0u + row0 * s0ld + col0;
 #pragma unroll
             for (int e = 0; e < R; ++e)
 #pragma unroll
                 for (int c = 0; c < CC; c += 4) {
-                    const float4 q = *reinterpret_cast<const float4 *>(src + e * N + c);
+                    const float4 q = *reinterpret_cast<const float4 *>(src + e * s0ld + c);
                     S[e][c] = q.x; S[e][c + 1] = q.y; S[e][c + 2] = q.z; S[e][c + 3] = q.w;
                 }
         } else {
@@ -339,12 +357,12 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
             __syncthreads();       // Y
         }
         if (sTu) {
-            float *dst = sTu + (int64_t)row0 * N + col0;
+            float *dst = sTu + row0 * sTld + col0;
 #pragma unroll
             for (int e = 0; e < R; ++e)
 #pragma unroll
                 for (int c = 0; c < CC; c += 4)
-                    *reinterpret_cast<float4 *>(dst + e * N + c) =
+                    *reinterpret_cast<float4 *>(dst + e * sTld + c) =
                         make_float4(S[e][c], S[e][c + 1], S[e][c + 2], S[e][c + 3]);
         }
         return;

@@ -21,14 +21,15 @@ constexpr int N = 64;
 
 // out = X B + C over 64 x 64 fp32 matrices, 256 threads: thread t owns row
 // t / 4, columns 16 (t % 4) .. + 15.  X and B are in LDS (B row-major);
-// C is read before out is written (they may be the same memory).
+// C and out have row stride ld, and C is read before out is written (they
+// may be the same memory).
 __device__ __forceinline__ void mma64(const float *X, const float *Bm, const float *C, float *out,
-                                      float *Xnext)
+                                      int64_t ld, float *Xnext)
 {
     const int t = threadIdx.x, i = t >> 2, j0 = 16 * (t & 3);
     float acc[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = C[i * N + j0 + j];
+    for (int j = 0; j < 16; ++j) acc[j] = C[i * ld + j0 + j];
     for (int k = 0; k < N; ++k) {
         const float x = X[i * N + k];
 #pragma unroll
@@ -37,27 +38,36 @@ __device__ __forceinline__ void mma64(const float *X, const float *Bm, const flo
     __syncthreads();   // every thread is done reading X and B
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        out[i * N + j0 + j] = acc[j];
+        out[i * ld + j0 + j] = acc[j];
         Xnext[i * N + j0 + j] = acc[j];
     }
 }
 
 // Forward: S_in(s + 1) = S_in(s) P_s + Q_s for s = 1 .. nseg - 2, where
-// S_in(1) = Q_0 is already in the checkpoint at segment 1's start and Q_s
-// is in the checkpoint at segment s + 1's start (overwritten with S_in(s+1)).
-__global__ void __launch_bounds__(256) compose_fwd_kernel(float *ckpt, const float *pbuf, int nck,
-                                                          int nseg, int nckseg)
+// S_in(1) = Q_0 is already in segment 1's carry slot and Q_s is in segment
+// s + 1's (overwritten with S_in(s + 1)).  The carry slot of segment s is
+// the checkpoint at its start, P_s in pbuf (row stride 64); without a
+// checkpoint record (ckpt null) they are the rows of steps 0 .. 63 and
+// 64 .. 127 of segment s in y (row stride H * 64).
+__global__ void __launch_bounds__(256) compose_fwd_kernel(float *ckpt, const float *pbuf, float *y,
+                                                          int64_t T, int64_t H, int nck, int nseg,
+                                                          int nckseg, int chunk)
 {
     __shared__ float X[N * N], Pm[N * N];
     const int64_t bh = blockIdx.x;
     const int t = threadIdx.x;
-    auto slot = [&](int s) { return ckpt + (bh * nck + (int64_t)s * nckseg) * N * N; };
-    for (int e = t; e < N * N; e += 256) X[e] = slot(1)[e];
+    const bool in_y = ckpt == nullptr;
+    const int64_t ld = in_y ? H * N : N;
+    auto slot = [&](int s) {
+        return in_y ? y + ((bh / H) * T * H + bh % H) * N + (int64_t)s * nckseg * chunk * ld
+                    : ckpt + (bh * nck + (int64_t)s * nckseg) * N * N;
+    };
+    for (int e = t; e < N * N; e += 256) X[e] = slot(1)[(e / N) * ld + e % N];
     for (int s = 1; s <= nseg - 2; ++s) {
-        const float *P = pbuf + (bh * nseg + s) * N * N;
-        for (int e = t; e < N * N; e += 256) Pm[e] = P[e];
+        const float *P = in_y ? slot(s) + N * ld : pbuf + (bh * nseg + s) * N * N;
+        for (int e = t; e < N * N; e += 256) Pm[e] = P[(e / N) * ld + e % N];
         __syncthreads();
-        mma64(X, Pm, slot(s + 1), slot(s + 1), X);
+        mma64(X, Pm, slot(s + 1), slot(s + 1), ld, X);
         __syncthreads();
     }
 }
@@ -75,7 +85,7 @@ __global__ void __launch_bounds__(256) compose_bwd_kernel(float *gbuf, const flo
         const float *P = pbuf + (bh * nseg + s) * N * N;
         for (int e = t; e < N * N; e += 256) Pt[(e % N) * N + e / N] = P[e];   // P^T
         __syncthreads();
-        mma64(X, Pt, G + (int64_t)s * N * N, G + (int64_t)s * N * N, X);
+        mma64(X, Pt, G + (int64_t)s * N * N, G + (int64_t)s * N * N, N, X);
         __syncthreads();
     }
 }
@@ -97,7 +107,7 @@ hipError_t launch_compose_forward(const FwdLaunch &a, hipStream_t stream)
     if (a.nseg < 3) return hipSuccess;   // S_in(1) = Q_0 is all there is
     const int nck = (int)((a.T + a.chunk - 1) / a.chunk);
     hipLaunchKernelGGL(compose_fwd_kernel, dim3((unsigned)(a.B * a.H)), dim3(256), 0, stream, a.ckpt,
-                       a.pbuf, nck, a.nseg, a.nckseg);
+                       a.pbuf, a.y, a.T, a.H, nck, a.nseg, a.nckseg, a.chunk);
     return hipGetLastError();
 }
 

@@ -96,3 +96,38 @@ def test_split_falls_back_per_head():
             same = all(torch.equal(a[n][b, :, h], s[n][b, :, h]) for n in H.GRADS) and \
                 torch.equal(a["ds0"][b, h], s["ds0"][b, h])
             assert same == ((b, h) in flagged), (b, h, same)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}_t{}_h{}_{}_s0{}_dsT{}".format(*c))
+def test_split_inference(case):
+    """The forward without a checkpoint record runs split with its carries in
+    y's rows: the same bits as the forward with a record, y prefilled with
+    NaN (every row is overwritten), against the oracle."""
+    B, T, Hh, dt, s0, _ = case
+    wl = custom(B, T, Hh, 64, dtype=dt, has_s0=s0, has_dsT=False, seed=800 + T)
+    _say(f"case split inference {wl.name}")
+    inp = make_inputs(wl, device="cuda")
+    y0 = torch.full((B, T, Hh, 64), float("nan"), device="cuda")
+    y, sT, _ = api.wkv7_forward(*(inp[n] for n in H.IN), inp["s0"], out=(y0, None, None))
+    yc, sTc, _ = api.wkv7_forward(*(inp[n] for n in H.IN), inp["s0"], want_ckpt=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yc) and torch.equal(sT, sTc)
+    sl = {n: H.to64(inp[n]) for n in H.IN}
+    import oracle
+    ry, rs = oracle.forward(*(sl[n] for n in H.IN), s0=H.to64(inp["s0"]))
+    _check({"y": y, "sT": sT}, {"y": ry, "sT": rs}, H.TAU[inp["r"].dtype], wl.name)
+
+
+def test_split_inference_fused_and_state_only():
+    """Fused inputs without a record (split, carries in y); and sT alone
+    (no y to hold the carries: one pass per (b, h))."""
+    wl = custom(1, 2048, 2, 64, has_s0=True, has_dsT=False, seed=43)
+    _say(f"case split inference fused {wl.name}")
+    inp = make_inputs(wl, device="cuda", fused=True)
+    y, sT, _ = api.wkv7_forward(*(inp[n] for n in H.IN), inp["s0"], fused=True)
+    _, sT2, _ = api.wkv7_forward(*(inp[n] for n in H.IN), inp["s0"], want_y=False, fused=True)
+    torch.cuda.synchronize()
+    sl = {n: H.to64(inp[n]) for n in H.IN}
+    ry, rs = OF.forward(*(sl[n] for n in H.IN), s0=H.to64(inp["s0"]))
+    _check({"y": y, "sT": sT}, {"y": ry, "sT": rs}, 2e-4, "split inference fused")
+    _check({"sT": sT2}, {"sT": rs}, 2e-4, "state only, fused")
