@@ -404,8 +404,10 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
         // The y and c tile of this wave: steps 16 tb .. 16 tb + 15 of the
         // block (lane: step 16 tb + 4 g + r), rows 16 ib .. 16 ib + 15 (lane:
         // row 16 ib + l16).  Its part of sum v kt^T: rows 16 ib .., column
-        // tiles 2 tb and 2 tb + 1.
-        constexpr int tb = h & 1, ib = h >> 1;
+        // tiles 2 tb and 2 tb + 1.  The second time block has twice the
+        // tiles of the first (u <= t); helpers h and h + 4 share a SIMD and
+        // take one of each.
+        constexpr int tb = (h ^ (h >> 2)) & 1, ib = h >> 1;
 
         // ---- lane offsets (floats) into the swizzled [rows][64] arrays:
         //   rows 16 X + l16, columns 16 q4 + 4 g .. + 3    L1[q4] + 1024 X
