@@ -261,7 +261,11 @@ __device__ __forceinline__ void wait_dma()
 // goes through M0).  Written as inline
 // asm so the compiler does not treat later LDS reads as possibly reading
 // this copy: it would otherwise wait for every copy in flight before each
-// LDS read.  Completion is awaited explicitly with wait_dma().
+// LDS read.  Completion is awaited explicitly with wait_dma().  M0 is listed
+// as clobbered; the compiler warns that it keeps no value of a reserved
+// register across inline asm, which costs nothing here: nothing else in
+// these kernels uses M0 (gfx950's LDS instructions do not take it), and in
+// the generated code every write of M0 is this one, right before its copy.
 __device__ __forceinline__ void dma16(const void *gsrc, const float *lds_wave_base)
 {
     const unsigned m0 = __builtin_amdgcn_readfirstlane(
