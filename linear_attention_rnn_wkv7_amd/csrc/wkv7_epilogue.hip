@@ -15,9 +15,11 @@
 // A row (b, t, h) is 64 contiguous floats: 16 lanes hold 4 each, and its
 // sums (mean, variance, bonus, the norm's backward terms) are DPP sums over
 // those 16 lanes, in a fixed order.  The backward's workgroups each keep one
-// head and a range of (b, t), add the parameter gradients of their rows in
-// registers and LDS in a fixed order, and a second kernel adds the
-// workgroups' partials in a fixed order: results are reproducible bit for bit.
+// head, or four adjacent heads when H is a multiple of 4 (so that four lane
+// groups read 1 KB of contiguous rows), and a range of (b, t); each lane
+// group keeps one head and adds the parameter gradients of its rows in
+// registers; LDS and a second kernel add the partials in a fixed order:
+// results are reproducible bit for bit.
 
 #include "wkv7_device.h"
 #include "wkv7_internal.h"
@@ -82,21 +84,23 @@ __global__ void __launch_bounds__(256) epi_fwd_kernel(EpiArgs<TIn> p)
     st4f(p.z + o, mul4(yb, g));
 }
 
-// Workgroup (h, c): rows (bt, h) for bt in chunk c, 16 at a time.
-template <typename TIn>
+// Workgroup (hg, c): heads HPW hg .. + HPW - 1, rows (bt, h) for bt in chunk
+// c; lane group grp takes head HPW hg + grp % HPW and every (16 / HPW)-th bt.
+template <typename TIn, int HPW>
 __global__ void __launch_bounds__(256) epi_bwd_kernel(EpiArgs<TIn> p)
 {
+    constexpr int kStep = 16 / HPW;   // lane groups per head
     __shared__ float red[16][3][N];
     const int t = threadIdx.x, l = t & 15, grp = t >> 4;
-    const int h = (int)(blockIdx.x / p.nchunk), c = (int)(blockIdx.x % p.nchunk);
+    const int hg = (int)(blockIdx.x / p.nchunk), c = (int)(blockIdx.x % p.nchunk);
+    const int h = HPW * hg + grp % HPW;
     const int po = h * N + 4 * l;
     const float4 lw = ld4f(p.ln_w + po), lb = ld4f(p.ln_b + po), rk = ld4f(p.r_k + po);
     float4 alw = make_float4(0.f, 0.f, 0.f, 0.f), alb = alw, ark = alw;   // parameter partials
     const int64_t bt0 = (int64_t)c * p.chunk_rows;
     int64_t bt1 = bt0 + p.chunk_rows;
     if (bt1 > p.bt) bt1 = p.bt;
-#pragma unroll 2
-    for (int64_t bt = bt0 + grp; bt < bt1; bt += 16) {
+    for (int64_t bt = bt0 + grp / HPW; bt < bt1; bt += kStep) {
         const int64_t o = (bt * p.H + h) * N + 4 * l;
         float rstd;
         const float4 yn = gn_norm(ld4f(p.y + o), rstd);
@@ -124,32 +128,45 @@ __global__ void __launch_bounds__(256) epi_bwd_kernel(EpiArgs<TIn> p)
         st4f(p.dy + o, make_float4(rstd * (dn.x - mdn - yn.x * mdnn), rstd * (dn.y - mdn - yn.y * mdnn),
                                    rstd * (dn.z - mdn - yn.z * mdnn), rstd * (dn.w - mdn - yn.w * mdnn)));
     }
-    // the 16 row groups' partials, added in a fixed order
+    // each head's row groups' partials, added in a fixed order
     st4f(&red[grp][0][4 * l], alw);
     st4f(&red[grp][1][4 * l], alb);
     st4f(&red[grp][2][4 * l], ark);
     __syncthreads();
-    if (t < 3 * N) {
-        const int kind = t / N, j = t % N;
+    for (int i = t; i < HPW * 3 * N; i += 256) {
+        const int sub = i / (3 * N), kind = (i / N) % 3, j = i % N;
         float acc = 0.f;
-        for (int q = 0; q < 16; ++q) acc += red[q][kind][j];
-        p.part[((int64_t)blockIdx.x * 3 + kind) * N + j] = acc;
+#pragma unroll
+        for (int q = 0; q < kStep; ++q) acc += red[q * HPW + sub][kind][j];
+        p.part[(((int64_t)(HPW * hg + sub) * p.nchunk + c) * 3 + kind) * N + j] = acc;
     }
 }
 
-// dln_w, dln_b, dr_k [H][64]: the workgroups' partials in chunk order.
-__global__ void epi_reduce_kernel(const float *part, float *dlw, float *dlb, float *drk, int64_t H,
-                                  int nchunk)
+// dln_w, dln_b, dr_k [H][64]: workgroup (h, kind) adds head h's partials
+// of one kind, the 16 waves each the chunks c = wave mod 16 (in chunk
+// order), then the 16 wave sums in wave order.
+__global__ void __launch_bounds__(1024) epi_reduce_kernel(const float *part, float *dlw, float *dlb,
+                                                           float *drk, int nchunk)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= 3 * H * N) return;
-    const int kind = (int)(i / (H * N));
-    const int64_t hj = i % (H * N), h = hj / N, j = hj % N;
+    __shared__ float red[16][N];
+    const int t = threadIdx.x, j = t & 63, wv = t >> 6;
+    const int64_t h = blockIdx.x;
+    const int kind = (int)blockIdx.y;
     float acc = 0.f;
-#pragma unroll 16
-    for (int c = 0; c < nchunk; ++c) acc += part[((h * nchunk + c) * 3 + kind) * N + j];
-    (kind == 0 ? dlw : kind == 1 ? dlb : drk)[hj] = acc;
+#pragma unroll 8
+    for (int c = wv; c < nchunk; c += 16) acc += part[((h * nchunk + c) * 3 + kind) * N + j];
+    red[wv][j] = acc;
+    __syncthreads();
+    if (t < N) {
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) sum += red[q][t];
+        (kind == 0 ? dlw : kind == 1 ? dlb : drk)[h * N + t] = sum;
+    }
 }
+
+// Heads per backward workgroup: 4 when H is a multiple of 4, else 1.
+int epi_hpw(int64_t H) { return H % 4 == 0 ? 4 : 1; }
 
 template <typename TIn>
 EpiArgs<TIn> epi_args(const EpiLaunch &a)
@@ -191,12 +208,16 @@ template <typename TIn>
 hipError_t launch_epi_bwd_t(const EpiLaunch &a, hipStream_t stream)
 {
     const EpiArgs<TIn> p = epi_args<TIn>(a);
-    hipLaunchKernelGGL(epi_bwd_kernel<TIn>, dim3((unsigned)(a.H * a.nchunk)), dim3(256), 0, stream, p);
+    const int hpw = epi_hpw(a.H);
+    const dim3 grid((unsigned)(a.H / hpw * a.nchunk));
+    if (hpw == 4)
+        hipLaunchKernelGGL((epi_bwd_kernel<TIn, 4>), grid, dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((epi_bwd_kernel<TIn, 1>), grid, dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n = 3 * a.H * N;
-    hipLaunchKernelGGL(epi_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.part,
-                       a.dln_w, a.dln_b, a.dr_k, a.H, a.nchunk);
+    hipLaunchKernelGGL(epi_reduce_kernel, dim3((unsigned)a.H, 3), dim3(1024), 0, stream, a.part, a.dln_w,
+                       a.dln_b, a.dr_k, a.nchunk);
     return hipGetLastError();
 }
 
@@ -204,9 +225,11 @@ hipError_t launch_epi_bwd_t(const EpiLaunch &a, hipStream_t stream)
 
 int epilogue_chunks(int64_t BT, int64_t H)
 {
-    // about 2048 workgroups in all, each with at least 16 rows
-    int64_t c = (2048 + H - 1) / H;
-    const int64_t most = (BT + 15) / 16;
+    // about 2048 workgroups in all (of 4 heads when H is a multiple of 4,
+    // else 1), each with at least one row per lane group
+    const int64_t hpw = epi_hpw(H);
+    int64_t c = (2048 * hpw + H - 1) / H;
+    const int64_t most = (BT + 16 / hpw - 1) / (16 / hpw);
     if (c > most) c = most;
     return (int)(c < 1 ? 1 : c);
 }

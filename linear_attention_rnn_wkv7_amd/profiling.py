@@ -22,7 +22,8 @@ import statistics
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 _CSRC = "linear_attention_rnn_wkv7_amd/csrc/"
 KERNEL_SOURCES = tuple(_CSRC + f for f in ("wkv7_bwd.hip", "wkv7_bwdc.hip", "wkv7_fwd.hip",
-                                           "wkv7_fwdc.hip", "wkv7_decode.hip", "wkv7_device.h"))
+                                           "wkv7_fwdc.hip", "wkv7_decode.hip", "wkv7_split.hip",
+                                           "wkv7_epilogue.hip", "wkv7_device.h"))
 # the sources each kernel is built from (its traffic record is stale once
 # one of them changes)
 _KERNEL_FILES = {
@@ -31,6 +32,8 @@ _KERNEL_FILES = {
     "wkv7_bwd_kernel": ("wkv7_bwd.hip", "wkv7_device.h"),
     "wkv7_fwd_kernel": ("wkv7_fwd.hip", "wkv7_device.h"),
     "wkv7_decode_kernel": ("wkv7_decode.hip", "wkv7_device.h"),
+    "epi_fwd_kernel": ("wkv7_epilogue.hip", "wkv7_device.h"),
+    "epi_bwd_kernel": ("wkv7_epilogue.hip", "wkv7_device.h"),
 }
 
 
