@@ -123,7 +123,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
 {
     constexpr int N = 64, R = 2, CC = 8, LPR = 8;
     __shared__ __align__(16) float slot[2][6][kTB * N];  // block inputs, by q & 1
-    __shared__ __align__(16) float gram[9][256];         // Gram tiles, lane-linear
+    __shared__ __align__(16) float gram[12][256];        // Gram tiles, lane-linear
     __shared__ __align__(16) float vkt[N * N];           // sum_u v_u kt_u^T, transposed
     __shared__ __align__(16) float sap[2][kTB * N];      // sa of the block, by q & 1
     __shared__ __align__(16) float sS0[N * N];           // state before the block
@@ -541,7 +541,9 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
         // ---- Gram tile n: kind n / 3 (0: kt . ab with u < t, 1: kt . rb,
         // 2: bt . rb, both u <= t), position n % 3 = (u-block, t-block)
         // (0,0), (0,1), (1,1); D[u][t] in the accumulator layout, stored
-        // lane-linear.  Wave h computes tile h; wave 4 also tile 8.
+        // lane-linear.  Helper h computes tile h, and helpers 4 .. 7 (one
+        // per SIMD) each a quarter of tile 8's sum over the 64 columns, into
+        // slots 8 .. 11, added where tile 8 is read.
         auto gram_tile = [&](const float *sb, auto nc) {
             constexpr int n = decltype(nc)::value, kind = n / 3, pos = n % 3;
             constexpr int ub = pos == 2 ? 1 : 0, tn = pos == 0 ? 0 : 1;
@@ -570,13 +572,33 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
             }
             *reinterpret_cast<f4 *>(&gram[n][4 * lane]) = acc;
         };
+        // quarter h - 4 of tile 8 (bt . rb, u <= t, position (1,1)): columns
+        // 16 (h - 4) .. + 15
+        auto gram_quarter = [&](const float *sb) {
+            constexpr int q4 = h - 4;
+            const float4 xq = lds4(sb + vB * 2048 + 1024, L1[q4]);
+            const float4 zq = lds4(sb + vR * 2048 + 1024, L1[q4]);
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mfma(xq.x, zq.x, acc);
+            acc = mfma(xq.y, zq.y, acc);
+            acc = mfma(xq.z, zq.z, acc);
+            acc = mfma(xq.w, zq.w, acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r - l16 > 0) acc[r] = 0.f;
+            *reinterpret_cast<f4 *>(&gram[8 + q4][4 * lane]) = acc;
+        };
         auto grams = [&](const float *sb) {
             gram_tile(sb, std::integral_constant<int, h>{});
-            if constexpr (h == 4) gram_tile(sb, std::integral_constant<int, 8>{});
+            if constexpr (h >= 4) gram_quarter(sb);
         };
         auto gram_get = [&](int kind, int ub) -> f4 {
             const int pos = tb == 0 ? 0 : 1 + ub;
-            return *reinterpret_cast<const f4 *>(&gram[3 * kind + pos][4 * lane]);
+            if (3 * kind + pos != 8) return *reinterpret_cast<const f4 *>(&gram[3 * kind + pos][4 * lane]);
+            f4 sum = *reinterpret_cast<const f4 *>(&gram[8][4 * lane]);
+#pragma unroll
+            for (int k = 9; k < 12; ++k) sum += *reinterpret_cast<const f4 *>(&gram[k][4 * lane]);
+            return sum;
         };
 
         f4 Y, Yv, VK[2], PbA[2], PbB[2], PbC[2];
