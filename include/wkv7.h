@@ -123,12 +123,13 @@ enum {
 /* Bytes of the checkpoint record for `shape`:
  * roundup(B*H*ceil(T/C)*N*N*4, 256) + B*T*H*N*4; 0 when the shape is invalid.
  * Shapes of few, long sequences run split into segments (N = 64, C = 64,
- * T*H*64*4 < 2^31, B*H <= 64, at least 16 chunks; the count, up to 8, and
+ * T*H*64*4 < 2^31, B*H <= 64, at least 4 chunks; the count, up to 8, and
  * the segment length follow from the shape): their record rounds the sa
  * part up to 256 bytes and adds the segments' transition products,
  * B*H*nseg*N*N*4 bytes.  A wkv7_forward with no record runs split when it
- * writes y, keeping the carries between segments in y's own rows until
- * the segments overwrite them with their outputs. */
+ * writes y and the last segment has at least N steps, keeping the carries
+ * between segments in y's own rows until the segments overwrite them with
+ * their outputs. */
 size_t wkv7_checkpoint_bytes(const wkv7_shape *shape);
 
 /* Bytes of device workspace wkv7_backward needs: the per-(b,h) state

@@ -19,7 +19,7 @@ struct Dims {
 };
 
 // Few, long sequences run in segments so that more workgroups than (b, h)
-// pairs fill the device: up to 8 segments of at least 8 chunks, while there
+// pairs fill the device: up to 8 segments of at least 2 chunks, while there
 // are at most 64 (b, h).  Needs the chunk forms (N = 64, C = 64).  Depends on
 // the shape only, so the forward's checkpoint record and the backward agree.
 void plan_split(Dims *d)
@@ -32,7 +32,7 @@ void plan_split(Dims *d)
         return;
     int64_t nseg = 256 / units;
     if (nseg > 8) nseg = 8;
-    if (nseg > d->nck / 8) nseg = d->nck / 8;
+    if (nseg > d->nck / 2) nseg = d->nck / 2;
     if (nseg < 2) return;
     const int64_t per = (d->nck + nseg - 1) / nseg;
     nseg = (d->nck + per - 1) / per;   // no empty segment
@@ -224,8 +224,8 @@ int wkv7_forward(const wkv7_shape *shape, const void *r, const void *w, const vo
     } else if (!ckpt && y && d.nseg > 1) {
         // no record: the carries go into the segments' own rows of y (a
         // state takes N steps of a (b, h), a carry and a transition product
-        // 2N; segments but the last have at least 8 chunks, and the last at
-        // least 2 under plan_split, so this check always passes)
+        // 2N; segments but the last have at least 2 chunks, and the last
+        // needs N steps, else the forward runs whole)
         if (d.T - (int64_t)(d.nseg - 1) * d.nckseg * d.C >= d.N) {
             L.nseg = d.nseg;
             L.nckseg = d.nckseg;

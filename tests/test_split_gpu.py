@@ -1,5 +1,5 @@
 """Few, long sequences run in segments (the library splits a shape with at
-most 64 (b, h) pairs into up to 8 segments of at least 8 chunks, carrying
+most 64 (b, h) pairs into up to 8 segments of at least 2 chunks, carrying
 states and state gradients between them): against the oracle, through the
 C ABI (MI355X only)."""
 import pytest
@@ -24,8 +24,9 @@ def _check(out, ref, tau, label):
     assert not bad, f"{label}: over {tau:g}*RMS: {bad} {errs}"
 
 
-# (B, T, H, dtype, s0, dsT): 2 segments; 8 segments of 8 chunks; 3 segments
-# with a ragged last chunk; bf16; a partial last 32-step block
+# (B, T, H, dtype, s0, dsT): 8 segments of 2 chunks; 8 of 8 chunks; 8 of 4
+# with a ragged last chunk; bf16 (8 of 3); 7 segments, the last one chunk of
+# 15 steps (a partial 32-step block; the forward without a record runs whole)
 CASES = [
     (1, 1024, 2, "f32", True, True),
     (1, 4096, 4, "f32", False, True),
@@ -84,7 +85,7 @@ def test_split_falls_back_per_head():
     _say(f"case split fallback {wl.name}")
     inp = make_inputs(wl, device="cuda")
     w = inp["w"]
-    w[1, 1000, 2, 7] = 0.0         # a decay of 0 in the second segment
+    w[1, 1000, 2, 7] = 0.0         # a decay of 0 in the sixth of 7 segments
     w[0, 100:120, 1, :] = 0.02     # decays below 1/16 in the first segment
     flagged = [(1, 2), (0, 1)]
     a = H.gpu_run(inp)
