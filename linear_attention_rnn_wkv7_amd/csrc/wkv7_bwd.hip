@@ -504,9 +504,10 @@ hipError_t launch_backward(const BwdLaunch &a, hipStream_t stream)
     const bool chunked = a.algo != 1 && chunked_backward_supported(a);
     if (a.fused && !chunked) return hipErrorInvalidValue;   // checked by the caller
     if (chunked && a.nseg > 1) {
-        // a split sequence: the later segments with their own gradients
-        // only, the carries, then the earlier segments with their incoming
-        // gradients; a head with any flagged segment is redone whole below
+        // a split sequence: the state gradients of the later segments from
+        // their own terms alone, the carries, then every segment with its
+        // incoming gradient; a head with any flagged segment is redone whole
+        // below
         hipError_t e = launch_backward_chunked(a, a.unit_flags, 1, stream);
         if (e == hipSuccess) e = launch_compose_backward(a, stream);
         if (e == hipSuccess) e = launch_backward_chunked(a, a.unit_flags, 2, stream);

@@ -207,9 +207,10 @@ struct BwdcArgs {
     int nck;
     // sequence split: mode 0 runs whole (b, h) sequences (one workgroup per
     // (b, h)); mode 1 (first pass) the segments s = 1 .. nseg - 1 of nckseg
-    // chunks each, with zero incoming gradient except the last and dL/d(the
-    // segment's initial state) to gbuf; mode 2 (second pass) the segments
-    // s = 0 .. nseg - 2 with the incoming gradient from gbuf[s + 1].
+    // chunks each, with zero incoming gradient except the last, forming only
+    // the state gradients (the dsa solve and the carry, no outputs) and
+    // dL/d(the segment's initial state) to gbuf; mode 2 (second pass) every
+    // segment with its incoming gradient (gbuf[s + 1], dsT for the last).
     int mode, nseg, nckseg;
     float *gbuf;   // [B*H][nseg][64][64]
 };
@@ -260,20 +261,22 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
     float *ds0u = p.ds0 ? p.ds0 + bh * 4096 : nullptr;
     int64_t fidx = bh;
     if (p.mode != 0) {
-        const int per = p.nseg - 1;
+        const int per = p.mode == 1 ? p.nseg - 1 : p.nseg;
         bh = (int64_t)blockIdx.x / per;
         seg = (int)((int64_t)blockIdx.x % per) + (p.mode == 1 ? 1 : 0);
         cb = seg * p.nckseg;
         ce = cb + p.nckseg < nck ? cb + p.nckseg : nck;
         fidx = bh * p.nseg + seg;
+        const float *dsT_real = p.dsT ? p.dsT + bh * 4096 : nullptr;
         if (p.mode == 1) {
-            dsTu = seg == p.nseg - 1 && p.dsT ? p.dsT + bh * 4096 : nullptr;
+            dsTu = seg == p.nseg - 1 ? dsT_real : nullptr;
             ds0u = p.gbuf + fidx * 4096;
         } else {
-            dsTu = p.gbuf + (fidx + 1) * 4096;
+            dsTu = seg == p.nseg - 1 ? dsT_real : p.gbuf + (fidx + 1) * 4096;
             ds0u = seg == 0 && p.ds0 ? p.ds0 + bh * 4096 : nullptr;
         }
     }
+    const bool full = p.mode != 1;   // the outputs, not only the state gradients
     const int64_t bidx = bh / H, head = bh % H;
     const int64_t stride = H * 64;
     const int64_t vbase = (bidx * T * H + head) * 64;
@@ -692,8 +695,10 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                     });
                 // the second-half waves' block inverses take longer than
                 // the right-hand side: two dsa-free products fit beside them
-                pd_xk();
-                pd_xv();
+                if (full) {
+                    pd_xk();
+                    pd_xv();
+                }
             } else {
                 const int slot = 10 + tix(fb, fb);
                 f4 X;
@@ -727,8 +732,10 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                 // T_fb[t][c] at tile position (t, c)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sTT[fb * 256 + A.pa[i]] = X[i];
-                pd_xk();
-                pd_xv();
+                if (full) {
+                    pd_xk();
+                    pd_xv();
+                }
             }
             __syncthreads();
             refresh();
@@ -746,7 +753,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                 };
                 // the dsa-free products fill the gaps of the dependent chain
                 apply_block(std::integral_constant<int, 3>{});
-                pd_xr();
+                if (full) pd_xr();
                 apply_block(std::integral_constant<int, 2>{});
                 apply_block(std::integral_constant<int, 1>{});
                 pd_h();
@@ -759,13 +766,13 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                         sD[A.col[i] + 1024 * tb] = t < Lc ? Rt[tb][i] : 0.f;
                     }
             } else {
-                pd_xr();
+                if (full) pd_xr();
                 pd_h();
             }
             __syncthreads();
             refresh();
             hprev_part(sD, sA);
-            rows2(XA, sD, s0B);    // S0^T dsa_t
+            if (full) rows2(XA, sD, s0B);    // S0^T dsa_t
             // c_j = sum_i (dL/dS0)[i][j] S0[i][j]: this wave's rows; ds0 after
             // the first chunk
             {
@@ -776,7 +783,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                     for (int i = 0; i < 4; ++i) cp = fmaf(Hn[lb][i], s0B[4 * (2 * HF + lb) + i], cp);
                 cp = swap_add16(cp, cp);
                 cp = swap_add32(cp, cp);
-                if (g == 0) sCj[HF][jw] = cp;
+                if (g == 0 && full) sCj[HF][jw] = cp;
                 if (c == cb && ds0u) {
 #pragma unroll
                     for (int lb = 0; lb < 2; ++lb)
@@ -790,10 +797,12 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             if (c > cb) issue_s0(c - 1);   // this chunk's S0 column is no longer needed
             // sa for the second pass, loaded while the first one runs
             float4 saR[2];
+            if (full) {
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
-                saR[m] = bload4(raw_buffer(p.sa + vbase, vext), (((uint32_t)t0 + t) * ustride + j4) * 4);
+                for (int m = 0; m < 2; ++m) {
+                    const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
+                    saR[m] = bload4(raw_buffer(p.sa + vbase, vext), (((uint32_t)t0 + t) * ustride + j4) * 4);
+                }
             }
 
             // One pass over the Grams of the value-side vectors in sVS (v,
@@ -845,14 +854,16 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 
             // ---- pass 1: Grams dy v^T, dsa v^T; dk bracket; kt terms of dr, da.
             // v is not read after the Grams: sa replaces it during the pass.
-            gram(sDY, sD, sVS, none);
+            if (full) gram(sDY, sD, sVS, none);
             __syncthreads();
             refresh();
-            value_terms(XK, sK);
+            if (full) {
+                value_terms(XK, sK);
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
-                put4(sVS, sw(t, j4), saR[m]);
+                for (int m = 0; m < 2; ++m) {
+                    const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
+                    put4(sVS, sw(t, j4), saR[m]);
+                }
             }
             __syncthreads();
             refresh();
@@ -865,7 +876,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             const BufRsrc odr = raw_buffer(p.dr + vbase, vext), oda = raw_buffer(p.da + vbase, vext);
             const BufRsrc odw = raw_buffer(p.dw + vbase, vext), odv = raw_buffer(p.dv + vbase, vext);
             auto ooff = [&](int t) { return (((uint32_t)t0 + t) * ustride + jw) * 4; };
-            gram(sDY, sD, sVS, [&](int k) {
+            if (full) gram(sDY, sD, sVS, [&](int k) {
                 if (k > 1) return;
                 const int tb = TB[k];
 #pragma unroll
@@ -877,18 +888,20 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             });
             __syncthreads();
             refresh();
-            rows2(XB, sVS, hB);    // Hb^T sa_t
-            value_terms(XB, sB);
             float f[2][4];
+            if (full) {
+                rows2(XB, sVS, hB);    // Hb^T sa_t
+                value_terms(XB, sB);
 #pragma unroll
-            for (int lt = 0; lt < 2; ++lt) {
+                for (int lt = 0; lt < 2; ++lt) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int o = A.col[i] + 1024 * TB[lt];
-                    f[lt][i] = sK[o] * XK[lt][i] + sB[o] * XB[lt][i] - sR[o] * XR[lt][i] -
-                               sA[o] * XA[lt][i];
+                    for (int i = 0; i < 4; ++i) {
+                        const int o = A.col[i] + 1024 * TB[lt];
+                        f[lt][i] = sK[o] * XK[lt][i] + sB[o] * XB[lt][i] - sR[o] * XR[lt][i] -
+                                   sA[o] * XA[lt][i];
+                    }
+                    sScan[fb][(4 * TB[lt] + g) * 16 + l16] = ((f[lt][0] + f[lt][1]) + f[lt][2]) + f[lt][3];
                 }
-                sScan[fb][(4 * TB[lt] + g) * 16 + l16] = ((f[lt][0] + f[lt][1]) + f[lt][2]) + f[lt][3];
             }
             __syncthreads();
             refresh();
@@ -956,7 +969,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                     ex += f[lt][i];
                 }
             };
-            gram(sR, sA, sK, outputs);
+            if (full) gram(sR, sA, sK, outputs);
             __syncthreads();
             refresh();
             // next chunk: r, w, a, b straight into their (now free) arrays
@@ -971,7 +984,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             sched_fence();
 
             // ---- dv = Hb kt_t + sum_{u>=t} dy_u (rb_u . kt_t) + sum_{u>t} dsa_u (ab_u . kt_t)
-            pipelined<16, 6>(
+            if (full) pipelined<16, 6>(
                 [&](int k, float (&b)[6]) {
                     const int ub = k >> 2, s = k & 3;
                     b[0] = colE(sDY, ub, s);
@@ -999,13 +1012,15 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             // them; the wait (for every earlier memory operation of the wave)
             // comes before dv's stores, so that it does not wait for them
             if (kDma && c > cb) wait_dma();
+            if (full) {
 #pragma unroll
-            for (int lt = 0; lt < 2; ++lt)
+                for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * TB[lt] + 4 * g + i;
-                    bstore(odv, ooff(t), XV[lt][i]);
-                }
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * TB[lt] + 4 * g + i;
+                        bstore(odv, ooff(t), XV[lt][i]);
+                    }
+            }
             __syncthreads();
             refresh();
         };
@@ -1046,7 +1061,7 @@ hipError_t launch_bwdc_t(const BwdLaunch &a, int *flags, int mode, hipStream_t s
     p.nseg = a.nseg;
     p.nckseg = a.nckseg;
     p.gbuf = a.gbuf;
-    const int64_t units = mode == 0 ? a.B * a.H : a.B * a.H * (a.nseg - 1);
+    const int64_t units = mode == 0 ? a.B * a.H : mode == 1 ? a.B * a.H * (a.nseg - 1) : a.B * a.H * a.nseg;
     hipLaunchKernelGGL((wkv7_bwdc_kernel<TIn, kFused>), dim3((unsigned)units), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
