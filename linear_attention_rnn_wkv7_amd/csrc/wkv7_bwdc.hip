@@ -229,7 +229,8 @@ __device__ __forceinline__ float bcast_group(float x)
     return __builtin_bit_cast(float, (G0 & 2) ? q[1] : q[0]);
 }
 
-template <typename TIn, bool kFused>
+// kLite: the split's first pass (mode 1), state gradients only
+template <typename TIn, bool kFused, bool kLite>
 __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 {
     // chunk vectors, [step][feature] swizzled: cumulative decay, rb, ab, kt,
@@ -276,7 +277,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             ds0u = seg == 0 && p.ds0 ? p.ds0 + bh * 4096 : nullptr;
         }
     }
-    const bool full = p.mode != 1;   // the outputs, not only the state gradients
+    constexpr bool full = !kLite;   // the outputs, not only the state gradients
     const int64_t bidx = bh / H, head = bh % H;
     const int64_t stride = H * 64;
     const int64_t vbase = (bidx * T * H + head) * 64;
@@ -695,7 +696,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                     });
                 // the second-half waves' block inverses take longer than
                 // the right-hand side: two dsa-free products fit beside them
-                if (full) {
+                if constexpr (full) {
                     pd_xk();
                     pd_xv();
                 }
@@ -732,7 +733,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                 // T_fb[t][c] at tile position (t, c)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sTT[fb * 256 + A.pa[i]] = X[i];
-                if (full) {
+                if constexpr (full) {
                     pd_xk();
                     pd_xv();
                 }
@@ -753,7 +754,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                 };
                 // the dsa-free products fill the gaps of the dependent chain
                 apply_block(std::integral_constant<int, 3>{});
-                if (full) pd_xr();
+                if constexpr (full) pd_xr();
                 apply_block(std::integral_constant<int, 2>{});
                 apply_block(std::integral_constant<int, 1>{});
                 pd_h();
@@ -766,13 +767,13 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                         sD[A.col[i] + 1024 * tb] = t < Lc ? Rt[tb][i] : 0.f;
                     }
             } else {
-                if (full) pd_xr();
+                if constexpr (full) pd_xr();
                 pd_h();
             }
             __syncthreads();
             refresh();
             hprev_part(sD, sA);
-            if (full) rows2(XA, sD, s0B);    // S0^T dsa_t
+            if constexpr (full) rows2(XA, sD, s0B);    // S0^T dsa_t
             // c_j = sum_i (dL/dS0)[i][j] S0[i][j]: this wave's rows; ds0 after
             // the first chunk
             {
@@ -797,7 +798,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             if (c > cb) issue_s0(c - 1);   // this chunk's S0 column is no longer needed
             // sa for the second pass, loaded while the first one runs
             float4 saR[2];
-            if (full) {
+            if constexpr (full) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     const int u = ltid + 512 * m, t = u >> 4, j4 = (u & 15) << 2;
@@ -854,10 +855,10 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
 
             // ---- pass 1: Grams dy v^T, dsa v^T; dk bracket; kt terms of dr, da.
             // v is not read after the Grams: sa replaces it during the pass.
-            if (full) gram(sDY, sD, sVS, none);
+            if constexpr (full) gram(sDY, sD, sVS, none);
             __syncthreads();
             refresh();
-            if (full) {
+            if constexpr (full) {
                 value_terms(XK, sK);
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
@@ -876,7 +877,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             const BufRsrc odr = raw_buffer(p.dr + vbase, vext), oda = raw_buffer(p.da + vbase, vext);
             const BufRsrc odw = raw_buffer(p.dw + vbase, vext), odv = raw_buffer(p.dv + vbase, vext);
             auto ooff = [&](int t) { return (((uint32_t)t0 + t) * ustride + jw) * 4; };
-            if (full) gram(sDY, sD, sVS, [&](int k) {
+            if constexpr (full) gram(sDY, sD, sVS, [&](int k) {
                 if (k > 1) return;
                 const int tb = TB[k];
 #pragma unroll
@@ -889,7 +890,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             __syncthreads();
             refresh();
             float f[2][4];
-            if (full) {
+            if constexpr (full) {
                 rows2(XB, sVS, hB);    // Hb^T sa_t
                 value_terms(XB, sB);
 #pragma unroll
@@ -969,7 +970,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                     ex += f[lt][i];
                 }
             };
-            if (full) gram(sR, sA, sK, outputs);
+            if constexpr (full) gram(sR, sA, sK, outputs);
             __syncthreads();
             refresh();
             // next chunk: r, w, a, b straight into their (now free) arrays
@@ -984,7 +985,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             sched_fence();
 
             // ---- dv = Hb kt_t + sum_{u>=t} dy_u (rb_u . kt_t) + sum_{u>t} dsa_u (ab_u . kt_t)
-            if (full) pipelined<16, 6>(
+            if constexpr (full) pipelined<16, 6>(
                 [&](int k, float (&b)[6]) {
                     const int ub = k >> 2, s = k & 3;
                     b[0] = colE(sDY, ub, s);
@@ -1012,7 +1013,7 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             // them; the wait (for every earlier memory operation of the wave)
             // comes before dv's stores, so that it does not wait for them
             if (kDma && c > cb) wait_dma();
-            if (full) {
+            if constexpr (full) {
 #pragma unroll
                 for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
@@ -1062,7 +1063,10 @@ hipError_t launch_bwdc_t(const BwdLaunch &a, int *flags, int mode, hipStream_t s
     p.nckseg = a.nckseg;
     p.gbuf = a.gbuf;
     const int64_t units = mode == 0 ? a.B * a.H : mode == 1 ? a.B * a.H * (a.nseg - 1) : a.B * a.H * a.nseg;
-    hipLaunchKernelGGL((wkv7_bwdc_kernel<TIn, kFused>), dim3((unsigned)units), dim3(512), 0, stream, p);
+    if (mode == 1)
+        hipLaunchKernelGGL((wkv7_bwdc_kernel<TIn, kFused, true>), dim3((unsigned)units), dim3(512), 0, stream, p);
+    else
+        hipLaunchKernelGGL((wkv7_bwdc_kernel<TIn, kFused, false>), dim3((unsigned)units), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
