@@ -146,6 +146,17 @@ def test_size_queries():
     assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == states + tape + 4 * 8 * 4096 * 4
     assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) == \
         4 * 7 * 64 * 64 * 4 + 256 + 256 + 4 * 8 * 4096 * 4
+    # segments of at least 2 chunks: 4 x 512 x 8 (32 heads, 8 chunks) runs
+    # in 4 segments, 4 x 256 x 8 in 2, and 4 x 192 x 8 (3 chunks) whole
+    st = 32 * 64 * 64 * 4   # one state per head
+    sh = _shape(B=4, T=512, H=8, N=64)
+    assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == 8 * st + 4 * 512 * 8 * 64 * 4 + 4 * st
+    assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) == 7 * st + 256 + 512 + 4 * st
+    sh = _shape(B=4, T=256, H=8, N=64)
+    assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == 4 * st + 4 * 256 * 8 * 64 * 4 + 2 * st
+    sh = _shape(B=4, T=192, H=8, N=64)
+    assert L.wkv7_checkpoint_bytes(ctypes.byref(sh)) == 3 * st + 4 * 192 * 8 * 64 * 4
+    assert L.wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) == 7 * st + 256
     assert L.wkv7_checkpoint_bytes(ctypes.byref(_shape(N=48))) == 0
     assert L.wkv7_checkpoint_bytes(None) == 0
 
