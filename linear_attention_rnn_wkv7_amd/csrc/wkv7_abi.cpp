@@ -224,9 +224,9 @@ int wkv7_forward(const wkv7_shape *shape, const void *r, const void *w, const vo
     } else if (!ckpt && y && d.nseg > 1) {
         // no record: the carries go into the segments' own rows of y (a
         // state takes N steps of a (b, h), a carry and a transition product
-        // 2N; segments but the last have at least 2 chunks, and the last
+        // 2N, which segments of at least 2 chunks hold; the last segment
         // needs N steps, else the forward runs whole)
-        if (d.T - (int64_t)(d.nseg - 1) * d.nckseg * d.C >= d.N) {
+        if ((int64_t)d.nckseg * d.C >= 2 * d.N && d.T - (int64_t)(d.nseg - 1) * d.nckseg * d.C >= d.N) {
             L.nseg = d.nseg;
             L.nckseg = d.nckseg;
         }
