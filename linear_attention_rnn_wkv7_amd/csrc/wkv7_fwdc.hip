@@ -118,7 +118,9 @@ struct FwdcArgs {
     float *pbuf;   // [B*H][nseg][64][64]; null when the carries live in y
 };
 
-template <typename TIn, bool kFused>
+// kLite: units that write no y (the split's first pass), which need
+// neither the y Gram tiles nor, with v = 0, c and sum v kt^T
+template <typename TIn, bool kFused, bool kLite>
 __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
 {
     constexpr int N = 64, R = 2, CC = 8, LPR = 8;
@@ -697,45 +699,80 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                 if (fastC) {
                     const float *sb = &slot[bn][0][0];
                     hsync();   // block q + 1 rescaled
-                    grams(sb);
-                    hsync();   // Gram tiles in LDS
-                    f4 Mk[2], Pk[2];
+                    f4 cacc = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (kLite) {
+                        // no y: only the kt . ab tiles (helpers 0-2) feed c; with
+                        // v = 0, c and sum v kt^T vanish and no tile is needed
+                        if constexpr (h < 3)
+                            if (!zero_v) gram_tile(sb, std::integral_constant<int, h>{});
+                        hsync();   // Gram tiles in LDS
+                        VK[0] = VK[1] = f4{0.f, 0.f, 0.f, 0.f};
+                        if (!zero_v) {
+                            f4 Mk[2];
+                            float vb[2][4], va[8], kb[8][2];
 #pragma unroll
-                    for (int ub = 0; ub <= tb; ++ub) {
-                        Mk[ub] = gram_get(0, ub);
-                        Pk[ub] = gram_get(1, ub);
-                        PbC[ub] = gram_get(2, ub);
-                    }
-                    // c (into the slot of w) and the v terms of y
-                    float vb[2][4];
+                            for (int ub = 0; ub <= tb; ++ub) {
+                                Mk[ub] = gram_get(0, ub);
 #pragma unroll
-                    for (int ub = 0; ub <= tb; ++ub)
+                                for (int r = 0; r < 4; ++r) vb[ub][r] = sb[vV * 2048 + 1024 * ub + L2[r]];
+                            }
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) vb[ub][r] = sb[vV * 2048 + 1024 * ub + L2[r]];
-                    // rows 16 ib .. 16 ib + 15 of sum_u v_u kt_u^T, column
-                    // tiles 2 tb, 2 tb + 1: operands
-                    float va[8], kb[8][2];
+                            for (int kk = 0; kk < 8; ++kk) {
+                                va[kk] = sb[vV * 2048 + L3 + 256 * kk + 16 * (ib ^ (kk & 3))];
 #pragma unroll
-                    for (int kk = 0; kk < 8; ++kk) {
-                        va[kk] = sb[vV * 2048 + L3 + 256 * kk + 16 * (ib ^ (kk & 3))];
+                                for (int m = 0; m < 2; ++m)
+                                    kb[kk][m] = sb[vK * 2048 + L3 + 256 * kk + 16 * ((2 * tb + m) ^ (kk & 3))];
+                            }
 #pragma unroll
-                        for (int m = 0; m < 2; ++m)
-                            kb[kk][m] = sb[vK * 2048 + L3 + 256 * kk + 16 * ((2 * tb + m) ^ (kk & 3))];
-                    }
-                    f4 cacc = {0.f, 0.f, 0.f, 0.f}, yacc = {0.f, 0.f, 0.f, 0.f};
+                            for (int ub = 0; ub <= tb; ++ub)
 #pragma unroll
-                    for (int ub = 0; ub <= tb; ++ub)
+                                for (int r = 0; r < 4; ++r) cacc = mfma(Mk[ub][r], vb[ub][r], cacc);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            cacc = mfma(Mk[ub][r], vb[ub][r], cacc);
-                            yacc = mfma(Pk[ub][r], vb[ub][r], yacc);
+                            for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                                for (int m = 0; m < 2; ++m) VK[m] = mfma(va[kk], kb[kk][m], VK[m]);
                         }
-                    VK[0] = VK[1] = f4{0.f, 0.f, 0.f, 0.f};
+                    } else {
+                        grams(sb);
+                        hsync();   // Gram tiles in LDS
+                        f4 Mk[2], Pk[2];
 #pragma unroll
-                    for (int kk = 0; kk < 8; ++kk)
+                        for (int ub = 0; ub <= tb; ++ub) {
+                            Mk[ub] = gram_get(0, ub);
+                            Pk[ub] = gram_get(1, ub);
+                            PbC[ub] = gram_get(2, ub);
+                        }
+                        // c (into the slot of w) and the v terms of y
+                        float vb[2][4];
 #pragma unroll
-                        for (int m = 0; m < 2; ++m) VK[m] = mfma(va[kk], kb[kk][m], VK[m]);
-                    Yv = yacc;
+                        for (int ub = 0; ub <= tb; ++ub)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) vb[ub][r] = sb[vV * 2048 + 1024 * ub + L2[r]];
+                        // rows 16 ib .. 16 ib + 15 of sum_u v_u kt_u^T, column
+                        // tiles 2 tb, 2 tb + 1: operands
+                        float va[8], kb[8][2];
+#pragma unroll
+                        for (int kk = 0; kk < 8; ++kk) {
+                            va[kk] = sb[vV * 2048 + L3 + 256 * kk + 16 * (ib ^ (kk & 3))];
+#pragma unroll
+                            for (int m = 0; m < 2; ++m)
+                                kb[kk][m] = sb[vK * 2048 + L3 + 256 * kk + 16 * ((2 * tb + m) ^ (kk & 3))];
+                        }
+                        f4 yacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ub = 0; ub <= tb; ++ub)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                cacc = mfma(Mk[ub][r], vb[ub][r], cacc);
+                                yacc = mfma(Pk[ub][r], vb[ub][r], yacc);
+                            }
+                        VK[0] = VK[1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                            for (int m = 0; m < 2; ++m) VK[m] = mfma(va[kk], kb[kk][m], VK[m]);
+                        Yv = yacc;
+                    }
                     float *cs = &slot[bn][vW][1024 * tb];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) cs[L2[r]] = cacc[r];
@@ -797,8 +834,12 @@ hipError_t launch_fwdc_t(const FwdLaunch &a, int mode, hipStream_t stream)
     p.pbuf = a.pbuf;
     const int64_t units = mode == 0 ? a.B * a.H
                         : mode == 1 ? a.B * a.H * (2 * a.nseg - 3) : a.B * a.H * a.nseg;
-    hipLaunchKernelGGL((wkv7_fwdc_kernel<TIn, kFused>), dim3((unsigned)units), dim3(kThreads), 0,
-                       stream, p);
+    if (mode == 1)
+        hipLaunchKernelGGL((wkv7_fwdc_kernel<TIn, kFused, true>), dim3((unsigned)units), dim3(kThreads), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((wkv7_fwdc_kernel<TIn, kFused, false>), dim3((unsigned)units), dim3(kThreads), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
