@@ -889,6 +889,21 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             });
             __syncthreads();
             refresh();
+            // fused inputs: the gate and the decay pre-activation at this
+            // lane's output steps, for the outputs after the next barrier
+            float gate[2][4], omg[2][4];
+            if constexpr (kFused && full) {
+                const BufRsrc rg = raw_buffer(p.b + vbase, vext * sizeof(TIn) / 4);
+                const BufRsrc rw = raw_buffer(p.w + vbase, vext * sizeof(TIn) / 4);
+#pragma unroll
+                for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t e = ((uint32_t)t0 + 16 * TB[lt] + 4 * g + i) * ustride + jw;
+                        gate[lt][i] = bload1<TIn>(rg, e);
+                        omg[lt][i] = bload1<TIn>(rw, e);
+                    }
+            }
             float f[2][4];
             if constexpr (full) {
                 rows2(XB, sVS, hB);    // Hb^T sa_t
@@ -918,17 +933,8 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
             // ---- outputs db, dr, da, dw (dw: prefix over steps of
             // k dk + b db - r dr - a da), beside the pass-3 Grams rb kt^T, ab kt^T
             float pre16[17];
-            float gate[2][4];   // fused inputs: the gate at this lane's output steps
             auto outputs = [&](int k) {
                 if (k == 0) {
-                    if constexpr (kFused) {
-                        const BufRsrc rg = raw_buffer(p.b + vbase, vext * sizeof(TIn) / 4);
-#pragma unroll
-                        for (int lt = 0; lt < 2; ++lt)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                gate[lt][i] = bload1<TIn>(rg, ((uint32_t)t0 + 16 * TB[lt] + 4 * g + i) * ustride + jw);
-                    }
                     // exclusive prefix of the 16 block sums of column jw (fixed order)
                     pre16[0] = 0.f;
 #pragma unroll
@@ -954,14 +960,17 @@ __global__ void __launch_bounds__(512) wkv7_bwdc_kernel(BwdcArgs<TIn> p)
                     const uint32_t off = ooff(t);
                     bstore(odr, off, XR[lt][i] * gt);
                     if constexpr (kFused) {
-                        // a = -kk: kk from ab = a g_{t-1}; ln w from w = g_t / g_{t-1}
+                        // a = -kk: kk from ab = a g_{t-1}.  d omega = (w dw) ln w
+                        // (1 - s) with ln w = -c s, s = sigmoid(omega), formed from
+                        // omega itself: ln(g_t / g_{t-1}) would lose its digits
+                        // as w nears 1
                         const float rgp = __builtin_amdgcn_rcpf(gp);
                         const float da_ = XA[lt][i] * gp, db_ = XB[lt][i] * inv;
                         const float kk = -sA[o] * rgp;
-                        const float lw = __builtin_amdgcn_logf(gt * rgp) * kLn2;   // ln w
+                        const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * omg[lt][i]));
                         bstore(odb, off, kk * db_);
                         bstore(oda, off, fmaf(gate[lt][i], db_, -da_));
-                        bstore(odw, off, wdw * lw * (1.f + lw * (1.f / kDecayCoeff)));
+                        bstore(odw, off, wdw * (-kDecayCoeff * sg) * (1.f - sg));
                     } else {
                         bstore(odb, off, XB[lt][i] * inv);
                         bstore(oda, off, XA[lt][i] * gp);

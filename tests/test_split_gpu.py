@@ -166,3 +166,32 @@ def test_split_slow_decay(case):
     yz, _ = oracle.forward(*(half[n] for n in H.IN))
     yt = ref["y"][:, T // 2:]
     assert np.abs(yz - yt).max() > 0.1 * np.sqrt(np.mean(yt * yt))
+
+
+def test_split_slow_decay_fused():
+    """Fused inputs with decay pre-activations near -6 (w = exp(-e^-0.5
+    sigmoid(omega)) ~ 0.9985): the carries matter, through the fused forms of
+    both passes of the split, against the fused oracle."""
+    wl = custom(1, 2048, 3, 64, has_s0=True, has_dsT=True, seed=61)
+    _say(f"case split slow decay fused {wl.name}")
+    inp = make_inputs(wl, device="cuda", fused=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(62)
+    inp["w"] = -6.0 + 0.5 * torch.randn(inp["w"].shape, generator=gen, device="cuda")
+    y, sT, ck = api.wkv7_forward(*(inp[n] for n in H.IN), inp["s0"], want_ckpt=True, fused=True)
+    g = api.wkv7_backward(*(inp[n] for n in H.IN), inp["dy"], inp["s0"], inp["dsT"], ck, fused=True)
+    yi, sTi, _ = api.wkv7_forward(*(inp[n] for n in H.IN), inp["s0"], fused=True)
+    torch.cuda.synchronize()
+    out = dict(g)
+    out["y"], out["sT"] = y, sT
+    sl = {n: H.to64(inp[n]) for n in H.IN + ("dy",)}
+    ry, rs = OF.forward(*(sl[n] for n in H.IN), s0=H.to64(inp["s0"]))
+    ref = OF.backward(*(sl[n] for n in H.IN), sl["dy"], s0=H.to64(inp["s0"]), dsT=H.to64(inp["dsT"]))
+    ref["y"], ref["sT"] = ry, rs
+    _check(out, ref, 2e-4, "split slow decay fused")
+    _check({"y": yi, "sT": sTi}, {"y": ry, "sT": rs}, 2e-4, "split slow decay fused, no record")
+    # the carry matters: the second half's y from a zero state is far off
+    half = {n: sl[n][:, 1024:] for n in H.IN}
+    yz, _ = OF.forward(*(half[n] for n in H.IN))
+    yt = ry[:, 1024:]
+    assert np.abs(yz - yt).max() > 0.1 * np.sqrt(np.mean(yt * yt))
