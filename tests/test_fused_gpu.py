@@ -117,3 +117,18 @@ def test_fused_matches_unfused_path():
                           {n: H.to64(x) for n, x in chained.items()}, 2e-4)
     _say("fused vs unfused: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     assert not bad, bad
+
+
+def test_fused_slow_decay_whole_sequences():
+    """Decay pre-activations near -6 (w ~ 0.9985) on a shape that runs one
+    workgroup per (b, h) (80 heads, no split): d omega is formed from omega,
+    not from the ratio of cumulative decays, and meets the bar."""
+    wl = custom(2, 300, 40, 64, has_s0=True, has_dsT=True, seed=71)
+    _say(f"case fused slow decay {wl.name}")
+    inp = make_inputs(wl, device="cuda", fused=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(72)
+    inp["w"] = -6.0 + 0.5 * torch.randn(inp["w"].shape, generator=gen, device="cuda")
+    out = _run(inp)
+    torch.cuda.synchronize()
+    _check(out, _oracle(inp), 2e-4, "fused slow decay")
