@@ -1,42 +1,112 @@
 /*
  * wkv7_oracle.c -- plain fp64 CPU oracle of the WKV7 (RWKV-7) recurrence and
- * of its reverse (backward-through-time) scan.
+ * of its exact gradient (backward through time).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
  * call this file: only the test suite, the smoke check and the CPU-baseline
  * leg of the benchmark use it.  It shares no code, header or table with the
  * HIP library.
  *
- * What is computed (Foundry page "rwkvx/rx_pretrain.c", functions
- * rx_wkv7_forward_seq and rx_wkv7_backward, and the comment block that
- * states the three reverse-scan steps), restated for one (batch b, head h)
- * with state S[i][j] (i = value/output row, j = key/input column):
+ * What is computed (Foundry page "rwkvx/rx_pretrain.c": the forward
+ * recurrence of rx_wkv7_forward_seq, and rx_wkv7_backward, whose result is
+ * the gradient of that forward), written as matrix operations for one
+ * (batch b, head h), state S in R^{N x N} (row i = value index, column
+ * j = key index), W_t = diag(w_t):
  *
- *   forward, t = 0 .. T-1, S starts at s0 (zeros when s0 is absent):
- *     sa[i]   = sum_j S[i][j] * a[j]                     (pre-update state)
- *     S[i][j] = S[i][j] * w[j] + v[i] * k[j] + sa[i] * b[j]
- *     y[i]    = sum_j S[i][j] * r[j]                     (post-update state)
- *   sT = S after the last step.
+ *   forward, t = 0 .. T-1, S_{-1} = s0 (zeros when absent):
+ *     S_t = S_{t-1} W_t + v_t k_t^T + (S_{t-1} a_t) b_t^T
+ *         = S_{t-1} M_t + v_t k_t^T,          M_t = W_t + a_t b_t^T
+ *     y_t = S_t r_t                            (the state after step t)
+ *   sT = S_{T-1}.
  *
- *   backward: G = dL/dS, seeded with dsT (zeros when absent -- the page seeds
- *   with zeros; a final-state gradient input is the extension the burn_mamba
- *   serial_recalculated backward.rs page makes with d_final_state), then for
- *   t = T-1 .. 0, with P = state before step t and St = state after it:
- *     (1) dr[j] = sum_i St[i][j] dy[i];          G[i][j] += dy[i] r[j]
- *     (2) dk[j] = sum_i G[i][j] v[i];  db[j] = sum_i G[i][j] sa[i]
- *         dw[j] = sum_i G[i][j] P[i][j]   (w is the multiplicative decay)
- *         dv[i] = sum_j G[i][j] k[j];  dsa[i] = sum_j G[i][j] b[j]
- *     (3) da[j] = sum_i dsa[i] P[i][j];  G[i][j] = G[i][j] w[j] + dsa[i] a[j]
- *   ds0 = G after t = 0.
+ *   backward: the gradient of L = sum_t <dy_t, y_t> + <dsT, sT> (dsT zeros
+ *   when absent -- the page starts from zeros; a final-state gradient input
+ *   is the extension the burn_mamba serial_recalculated backward.rs page
+ *   makes with d_final_state).  With G = dL/dS_t, reverse-mode through the
+ *   two lines above gives, for t = T-1 .. 0:
+ *     dr_t = S_t^T dy_t                        (from y_t = S_t r_t)
+ *     G   += dy_t r_t^T
+ *     dv_t = G k_t,   dk_t = G^T v_t           (from v_t k_t^T)
+ *     dM   = S_{t-1}^T G                       (from S_{t-1} M_t), so
+ *       dw_t = diag(dM)           i.e. dw_t[j] = sum_i S_{t-1}[i][j] G[i][j]
+ *       da_t = dM b_t             = S_{t-1}^T (G b_t)
+ *       db_t = dM^T a_t           = G^T (S_{t-1} a_t)
+ *     dL/dS_{t-1} = G M_t^T = G W_t + (G b_t) a_t^T
+ *   ds0 = dL/dS_{-1}.  w is the multiplicative decay itself (not a log).
  *
- * Layout: vectors [B][T][H][N], states [B][H][N][N] row-major, all fp64.
- * The backward caches every pre-step state of one (b,h) (T*N*N doubles), as
- * the page does; (b,h) pairs are independent and are spread over threads.
+ * Memory: the backward needs S_{t-1} and S_t for every t, in reverse.  It
+ * keeps the state before every REPLAY-th step from one forward pass, then
+ * for each such stretch, last first, replays the forward from that kept
+ * state (the same operations on the same numbers, so the same doubles) and
+ * holds the stretch's states.  That bounds memory by (T/REPLAY + REPLAY)
+ * states per thread without changing any arithmetic.
+ *
+ * Layout: vectors [B][T][H][N] (one step of one (b,h) is N contiguous
+ * values), states [B][H][N][N] row-major, all fp64.  (b,h) pairs are
+ * independent and are spread over threads.
  */
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 #include <pthread.h>
+
+enum { REPLAY = 64 };
+
+/* ------------------------------------------------------------------ */
+/* Matrix helpers: N x N row-major matrices, N-vectors.               */
+
+/* out = M x */
+static void mat_vec(const double *M, const double *x, double *out, int64_t N)
+{
+    for (int64_t i = 0; i < N; i++) {
+        double s = 0.0;
+        for (int64_t j = 0; j < N; j++) s += M[i * N + j] * x[j];
+        out[i] = s;
+    }
+}
+
+/* out = M^T x */
+static void mat_t_vec(const double *M, const double *x, double *out, int64_t N)
+{
+    for (int64_t j = 0; j < N; j++) {
+        double s = 0.0;
+        for (int64_t i = 0; i < N; i++) s += M[i * N + j] * x[i];
+        out[j] = s;
+    }
+}
+
+/* M = M diag(d) */
+static void scale_cols(double *M, const double *d, int64_t N)
+{
+    for (int64_t i = 0; i < N; i++)
+        for (int64_t j = 0; j < N; j++) M[i * N + j] *= d[j];
+}
+
+/* M = M + u x^T */
+static void add_outer(double *M, const double *u, const double *x, int64_t N)
+{
+    for (int64_t i = 0; i < N; i++)
+        for (int64_t j = 0; j < N; j++) M[i * N + j] += u[i] * x[j];
+}
+
+/* out[j] = sum_i A[i][j] B[i][j], the diagonal of A^T B */
+static void diag_t_prod(const double *A, const double *B, double *out, int64_t N)
+{
+    for (int64_t j = 0; j < N; j++) {
+        double s = 0.0;
+        for (int64_t i = 0; i < N; i++) s += A[i * N + j] * B[i * N + j];
+        out[j] = s;
+    }
+}
+
+/* dst = src (N x N), or zeros when src is NULL */
+static void copy_or_zero(double *dst, const double *src, int64_t N)
+{
+    if (src) memcpy(dst, src, (size_t)(N * N) * sizeof(double));
+    else memset(dst, 0, (size_t)(N * N) * sizeof(double));
+}
+
+/* ------------------------------------------------------------------ */
 
 typedef struct {
     const double *r, *w, *k, *v, *a, *b, *dy, *s0, *dsT;
@@ -47,14 +117,16 @@ typedef struct {
     pthread_mutex_t lock;
 } job_t;
 
-static inline size_t vix(const job_t *J, int64_t b, int64_t t, int64_t h, int64_t n)
+/* Offset of the N-vector of (b, t, h) in a [B][T][H][N] tensor. */
+static inline size_t vec_at(const job_t *J, int64_t b, int64_t t, int64_t h)
 {
-    return (size_t)(((b * J->T + t) * J->H + h) * J->N + n);
+    return (size_t)(((b * J->T + t) * J->H + h) * J->N);
 }
 
-static inline size_t six(const job_t *J, int64_t b, int64_t h, int64_t i, int64_t j)
+/* Offset of the N x N state of (b, h) in a [B][H][N][N] tensor. */
+static inline size_t state_at(const job_t *J, int64_t b, int64_t h)
 {
-    return (size_t)(((b * J->H + h) * J->N + i) * J->N + j);
+    return (size_t)((b * J->H + h) * J->N * J->N);
 }
 
 static int take_unit(job_t *J, int64_t *unit)
@@ -73,61 +145,36 @@ static void fail(job_t *J)
     pthread_mutex_unlock(&J->lock);
 }
 
-/* Load the initial state of (b,h) into S (N*N), zeros when s0 is absent. */
-static void load_s0(const job_t *J, int64_t b, int64_t h, double *S)
+/* One forward step at offset o of the vector tensors:
+ * S <- S W + v k^T + (S a) b^T, in place; sa is scratch (N). */
+static void step(const job_t *J, size_t o, double *S, double *sa)
 {
     const int64_t N = J->N;
-    for (int64_t i = 0; i < N; i++)
-        for (int64_t j = 0; j < N; j++)
-            S[i * N + j] = J->s0 ? J->s0[six(J, b, h, i, j)] : 0.0;
-}
-
-/* One forward step of (b,h) at time t, in place on S; writes sa (N) and,
- * when y_out is non-NULL, y (N values at y_out). */
-static void step_forward(const job_t *J, int64_t b, int64_t t, int64_t h,
-                         double *S, double *sa, double *y_out)
-{
-    const int64_t N = J->N;
-    for (int64_t i = 0; i < N; i++) {
-        double acc = 0.0;
-        for (int64_t j = 0; j < N; j++)
-            acc += S[i * N + j] * J->a[vix(J, b, t, h, j)];
-        sa[i] = acc;
-    }
-    for (int64_t i = 0; i < N; i++) {
-        const double vi = J->v[vix(J, b, t, h, i)];
-        double yy = 0.0;
-        for (int64_t j = 0; j < N; j++) {
-            const size_t q = vix(J, b, t, h, j);
-            S[i * N + j] = S[i * N + j] * J->w[q] + vi * J->k[q] + sa[i] * J->b[q];
-            yy += S[i * N + j] * J->r[q];
-        }
-        if (y_out) y_out[i] = yy;
-    }
+    mat_vec(S, J->a + o, sa, N);
+    scale_cols(S, J->w + o, N);
+    add_outer(S, J->v + o, J->k + o, N);
+    add_outer(S, sa, J->b + o, N);
 }
 
 static void *forward_worker(void *arg)
 {
     job_t *J = (job_t *)arg;
     const int64_t N = J->N;
-    double *S = (double *)malloc((size_t)N * N * sizeof(double));
+    double *S = (double *)malloc((size_t)(N * N) * sizeof(double));
     double *sa = (double *)malloc((size_t)N * sizeof(double));
-    double *yt = (double *)malloc((size_t)N * sizeof(double));
-    if (!S || !sa || !yt) { fail(J); free(S); free(sa); free(yt); return NULL; }
+    if (!S || !sa) { fail(J); free(S); free(sa); return NULL; }
     int64_t u;
     while (take_unit(J, &u)) {
         const int64_t b = u / J->H, h = u % J->H;
-        load_s0(J, b, h, S);
+        copy_or_zero(S, J->s0 ? J->s0 + state_at(J, b, h) : NULL, N);
         for (int64_t t = 0; t < J->T; t++) {
-            step_forward(J, b, t, h, S, sa, yt);
-            if (J->y)
-                for (int64_t i = 0; i < N; i++) J->y[vix(J, b, t, h, i)] = yt[i];
+            const size_t o = vec_at(J, b, t, h);
+            step(J, o, S, sa);
+            if (J->y) mat_vec(S, J->r + o, J->y + o, N);
         }
-        if (J->sT)
-            for (int64_t i = 0; i < N; i++)
-                for (int64_t j = 0; j < N; j++) J->sT[six(J, b, h, i, j)] = S[i * N + j];
+        if (J->sT) memcpy(J->sT + state_at(J, b, h), S, (size_t)(N * N) * sizeof(double));
     }
-    free(S); free(sa); free(yt);
+    free(S); free(sa);
     return NULL;
 }
 
@@ -135,96 +182,62 @@ static void *backward_worker(void *arg)
 {
     job_t *J = (job_t *)arg;
     const int64_t N = J->N, T = J->T, NN = N * N;
-    double *S = (double *)malloc((size_t)NN * sizeof(double));
-    double *St = (double *)malloc((size_t)NN * sizeof(double));
+    const int64_t nkeep = (T + REPLAY - 1) / REPLAY;
+    double *keep = (double *)malloc((size_t)((nkeep > 0 ? nkeep : 1) * NN) * sizeof(double));
+    double *hist = (double *)malloc((size_t)((REPLAY + 1) * NN) * sizeof(double));
     double *G = (double *)malloc((size_t)NN * sizeof(double));
-    double *dsa = (double *)malloc((size_t)N * sizeof(double));
-    double *Pc = (double *)malloc((size_t)(T > 0 ? T : 1) * NN * sizeof(double));
-    double *sac = (double *)malloc((size_t)(T > 0 ? T : 1) * N * sizeof(double));
-    if (!S || !St || !G || !dsa || !Pc || !sac) {
+    double *u = (double *)malloc((size_t)N * sizeof(double));
+    double *sa = (double *)malloc((size_t)N * sizeof(double));
+    if (!keep || !hist || !G || !u || !sa) {
         fail(J);
-        free(S); free(St); free(G); free(dsa); free(Pc); free(sac);
+        free(keep); free(hist); free(G); free(u); free(sa);
         return NULL;
     }
-    int64_t u;
-    while (take_unit(J, &u)) {
-        const int64_t b = u / J->H, h = u % J->H;
-        /* forward, keeping every pre-step state and every sa */
-        load_s0(J, b, h, S);
+    int64_t unit;
+    while (take_unit(J, &unit)) {
+        const int64_t b = unit / J->H, h = unit % J->H;
+        /* forward pass keeping the state before steps 0, REPLAY, 2 REPLAY, ... */
+        double *S = hist;
+        copy_or_zero(S, J->s0 ? J->s0 + state_at(J, b, h) : NULL, N);
         for (int64_t t = 0; t < T; t++) {
-            memcpy(Pc + (size_t)t * NN, S, (size_t)NN * sizeof(double));
-            step_forward(J, b, t, h, S, sac + (size_t)t * N, NULL);
+            if (t % REPLAY == 0) memcpy(keep + (t / REPLAY) * NN, S, (size_t)NN * sizeof(double));
+            step(J, vec_at(J, b, t, h), S, sa);
         }
-        /* seed */
-        for (int64_t i = 0; i < N; i++)
-            for (int64_t j = 0; j < N; j++)
-                G[i * N + j] = J->dsT ? J->dsT[six(J, b, h, i, j)] : 0.0;
-        /* reverse scan */
-        for (int64_t t = T - 1; t >= 0; t--) {
-            const double *P = Pc + (size_t)t * NN;
-            const double *sa = sac + (size_t)t * N;
-            /* state after step t, rebuilt from the cached pre-step state */
-            for (int64_t i = 0; i < N; i++) {
-                const double vi = J->v[vix(J, b, t, h, i)];
-                for (int64_t j = 0; j < N; j++) {
-                    const size_t q = vix(J, b, t, h, j);
-                    St[i * N + j] = P[i * N + j] * J->w[q] + vi * J->k[q] + sa[i] * J->b[q];
-                }
+        /* G = dL/dS_{T-1} */
+        copy_or_zero(G, J->dsT ? J->dsT + state_at(J, b, h) : NULL, N);
+        for (int64_t c = nkeep - 1; c >= 0; c--) {
+            const int64_t t0 = c * REPLAY, t1 = t0 + REPLAY < T ? t0 + REPLAY : T;
+            /* hist[s] = S_{t0+s-1}: the state before step t0+s, s = 0 .. t1-t0 */
+            memcpy(hist, keep + c * NN, (size_t)NN * sizeof(double));
+            for (int64_t t = t0; t < t1; t++) {
+                double *next = hist + (t - t0 + 1) * NN;
+                memcpy(next, hist + (t - t0) * NN, (size_t)NN * sizeof(double));
+                step(J, vec_at(J, b, t, h), next, sa);
             }
-            /* (1) read-out */
-            for (int64_t j = 0; j < N; j++) {
-                double acc = 0.0;
-                for (int64_t i = 0; i < N; i++)
-                    acc += St[i * N + j] * J->dy[vix(J, b, t, h, i)];
-                J->dr[vix(J, b, t, h, j)] = acc;
+            for (int64_t t = t1 - 1; t >= t0; t--) {
+                const size_t o = vec_at(J, b, t, h);
+                const double *Sprev = hist + (t - t0) * NN;     /* S_{t-1} */
+                const double *Scur = hist + (t - t0 + 1) * NN;  /* S_t */
+                /* y_t = S_t r_t */
+                mat_t_vec(Scur, J->dy + o, J->dr + o, N);
+                add_outer(G, J->dy + o, J->r + o, N);
+                /* v_t k_t^T */
+                mat_vec(G, J->k + o, J->dv + o, N);
+                mat_t_vec(G, J->v + o, J->dk + o, N);
+                /* S_{t-1} M_t with M_t = W_t + a_t b_t^T */
+                diag_t_prod(Sprev, G, J->dw + o, N);
+                mat_vec(G, J->b + o, u, N);
+                mat_t_vec(Sprev, u, J->da + o, N);
+                mat_vec(Sprev, J->a + o, sa, N);
+                mat_t_vec(G, sa, J->db + o, N);
+                /* G <- G M_t^T = G W_t + (G b_t) a_t^T */
+                scale_cols(G, J->w + o, N);
+                add_outer(G, u, J->a + o, N);
             }
-            for (int64_t i = 0; i < N; i++) {
-                const double dyi = J->dy[vix(J, b, t, h, i)];
-                for (int64_t j = 0; j < N; j++)
-                    G[i * N + j] += dyi * J->r[vix(J, b, t, h, j)];
-            }
-            /* (2) update gradients */
-            for (int64_t j = 0; j < N; j++) {
-                double gk = 0.0, gb = 0.0, gw = 0.0;
-                for (int64_t i = 0; i < N; i++) {
-                    const double g = G[i * N + j];
-                    gk += g * J->v[vix(J, b, t, h, i)];
-                    gb += g * sa[i];
-                    gw += g * P[i * N + j];
-                }
-                const size_t q = vix(J, b, t, h, j);
-                J->dk[q] = gk;
-                J->db[q] = gb;
-                J->dw[q] = gw;
-            }
-            for (int64_t i = 0; i < N; i++) {
-                double gv = 0.0, gs = 0.0;
-                for (int64_t j = 0; j < N; j++) {
-                    const size_t q = vix(J, b, t, h, j);
-                    gv += G[i * N + j] * J->k[q];
-                    gs += G[i * N + j] * J->b[q];
-                }
-                J->dv[vix(J, b, t, h, i)] = gv;
-                dsa[i] = gs;
-            }
-            /* (3) in-context term and carry to t-1 */
-            for (int64_t j = 0; j < N; j++) {
-                double acc = 0.0;
-                for (int64_t i = 0; i < N; i++)
-                    acc += dsa[i] * P[i * N + j];
-                J->da[vix(J, b, t, h, j)] = acc;
-            }
-            for (int64_t i = 0; i < N; i++)
-                for (int64_t j = 0; j < N; j++) {
-                    const size_t q = vix(J, b, t, h, j);
-                    G[i * N + j] = G[i * N + j] * J->w[q] + dsa[i] * J->a[q];
-                }
         }
-        if (J->ds0)
-            for (int64_t i = 0; i < N; i++)
-                for (int64_t j = 0; j < N; j++) J->ds0[six(J, b, h, i, j)] = G[i * N + j];
+        if (J->ds0) memcpy(J->ds0 + state_at(J, b, h), G, (size_t)NN * sizeof(double));
     }
-    free(S); free(St); free(G); free(dsa); free(Pc); free(sac);
+    free(keep); free(hist); free(G); free(u); free(sa);
     return NULL;
 }
 

@@ -249,6 +249,13 @@ def pin_torch_autograd(rng, lib=None, B=1, T=6, H=2, N=4):
     return max(errs)
 
 
+def pin_torch_autograd_long(rng, lib=None):
+    """The same check over 150 steps: the oracle's backward replays the
+    forward in stretches of 64 steps from kept states, so a sequence of two
+    whole stretches and a ragged third pins the replay bookkeeping."""
+    return pin_torch_autograd(rng, lib, B=1, T=150, H=2, N=3)
+
+
 # ------------------------------------------- exact rational forward mode
 class Dual:
     """a + b*eps with eps^2 = 0, over exact rationals."""
@@ -449,6 +456,7 @@ ALL_PINS = {
     "finite_differences": (pin_finite_differences, 1e-7),
     "identities": (pin_identities, 1e-11),
     "torch_autograd": (pin_torch_autograd, 1e-12),
+    "torch_autograd_long": (pin_torch_autograd_long, 1e-11),
     "exact_rational": (pin_exact_rational, 1e-13),
     "fused_finite_differences": (pin_fused_finite_differences, 1e-7),
     "fused_torch_autograd": (pin_fused_torch_autograd, 1e-12),

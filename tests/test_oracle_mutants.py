@@ -1,6 +1,7 @@
 """Plant plausible mistakes in copies of the oracle (on the CPU) and check
 that the pins catch every one: a transposed index, a wrong sign, a dropped
-term, the wrong state in a gradient, a seed that ignores dsT."""
+term, the wrong state in a gradient, a seed that ignores dsT, a slip in the
+backward's replay of the forward from kept states."""
 import os
 
 import numpy as np
@@ -13,35 +14,41 @@ import oracle_pins as P
 SRC = os.path.join(os.path.dirname(oracle.__file__), "wkv7_oracle.c")
 
 MUTANTS = {
-    "sa_transposed": ("acc += S[i * N + j] * J->a[vix(J, b, t, h, j)];",
-                      "acc += S[j * N + i] * J->a[vix(J, b, t, h, j)];"),
-    "update_sign": ("vi * J->k[q] + sa[i] * J->b[q];\n            yy",
-                    "vi * J->k[q] - sa[i] * J->b[q];\n            yy"),
-    "update_drops_vk": ("S[i * N + j] * J->w[q] + vi * J->k[q] + sa[i] * J->b[q];\n            yy",
-                        "S[i * N + j] * J->w[q] + sa[i] * J->b[q];\n            yy"),
-    "readout_pre_update": ("yy += S[i * N + j] * J->r[q];",
-                           "yy += (S[i * N + j] - vi * J->k[q]) * J->r[q];"),
-    "dr_uses_pre_state": ("acc += St[i * N + j] * J->dy[vix(J, b, t, h, i)];",
-                          "acc += P[i * N + j] * J->dy[vix(J, b, t, h, i)];"),
-    "dw_uses_post_state": ("gw += g * P[i * N + j];", "gw += g * St[i * N + j];"),
-    "db_uses_v": ("gb += g * sa[i];", "gb += g * J->v[vix(J, b, t, h, i)];"),
-    "dv_uses_b": ("gv += G[i * N + j] * J->k[q];", "gv += G[i * N + j] * J->b[q];"),
-    "da_transposed": ("acc += dsa[i] * P[i * N + j];", "acc += dsa[i] * P[j * N + i];"),
-    "carry_uses_b": ("G[i * N + j] * J->w[q] + dsa[i] * J->a[q];",
-                     "G[i * N + j] * J->w[q] + dsa[i] * J->b[q];"),
-    "carry_drops_decay": ("G[i * N + j] * J->w[q] + dsa[i] * J->a[q];",
-                          "G[i * N + j] + dsa[i] * J->a[q];"),
-    "dy_r_not_folded": ("G[i * N + j] += dyi * J->r[vix(J, b, t, h, j)];",
-                        "G[i * N + j] += 0.0 * dyi * J->r[vix(J, b, t, h, j)];"),
-    "seed_ignores_dsT": ("J->dsT ? J->dsT[six(J, b, h, i, j)] : 0.0",
-                         "0.0 * (J->dsT ? J->dsT[six(J, b, h, i, j)] : 0.0)"),
-    "s0_transposed": ("S[i * N + j] = J->s0 ? J->s0[six(J, b, h, i, j)] : 0.0;",
-                      "S[i * N + j] = J->s0 ? J->s0[six(J, b, h, j, i)] : 0.0;"),
+    "sa_transposed": ("mat_vec(S, J->a + o, sa, N);", "mat_t_vec(S, J->a + o, sa, N);"),
+    "update_sign": ("add_outer(S, sa, J->b + o, N);",
+                    "for (int64_t i = 0; i < N; i++) sa[i] = -sa[i]; add_outer(S, sa, J->b + o, N);"),
+    "update_drops_vk": ("    add_outer(S, J->v + o, J->k + o, N);\n", ""),
+    "readout_pre_update": ("step(J, o, S, sa);\n            if (J->y) mat_vec(S, J->r + o, J->y + o, N);",
+                           "if (J->y) mat_vec(S, J->r + o, J->y + o, N);\n            step(J, o, S, sa);"),
+    "dr_uses_pre_state": ("mat_t_vec(Scur, J->dy + o, J->dr + o, N);",
+                          "mat_t_vec(Sprev, J->dy + o, J->dr + o, N);"),
+    "dw_uses_post_state": ("diag_t_prod(Sprev, G, J->dw + o, N);",
+                           "diag_t_prod(Scur, G, J->dw + o, N);"),
+    "db_uses_v": ("mat_t_vec(G, sa, J->db + o, N);", "mat_t_vec(G, J->v + o, J->db + o, N);"),
+    "dv_uses_b": ("mat_vec(G, J->k + o, J->dv + o, N);", "mat_vec(G, J->b + o, J->dv + o, N);"),
+    "dk_transposed": ("mat_t_vec(G, J->v + o, J->dk + o, N);",
+                      "mat_vec(G, J->v + o, J->dk + o, N);"),
+    "da_transposed": ("mat_t_vec(Sprev, u, J->da + o, N);", "mat_vec(Sprev, u, J->da + o, N);"),
+    "carry_uses_b": ("add_outer(G, u, J->a + o, N);", "add_outer(G, u, J->b + o, N);"),
+    "carry_drops_decay": ("scale_cols(G, J->w + o, N);", "(void)0;"),
+    "dy_r_not_folded": ("add_outer(G, J->dy + o, J->r + o, N);", "(void)0;"),
+    "seed_ignores_dsT": ("copy_or_zero(G, J->dsT ? J->dsT + state_at(J, b, h) : NULL, N);",
+                         "copy_or_zero(G, NULL, N);"),
+    "state_transposed": ("if (src) memcpy(dst, src, (size_t)(N * N) * sizeof(double));",
+                         "if (src) { for (int64_t i = 0; i < N; i++) for (int64_t j = 0; j < N; j++) "
+                         "dst[i * N + j] = src[j * N + i]; }"),
+    "replay_keeps_post_state": (
+        "if (t % REPLAY == 0) memcpy(keep + (t / REPLAY) * NN, S, (size_t)NN * sizeof(double));\n"
+        "            step(J, vec_at(J, b, t, h), S, sa);",
+        "step(J, vec_at(J, b, t, h), S, sa);\n"
+        "            if (t % REPLAY == 0) memcpy(keep + (t / REPLAY) * NN, S, (size_t)NN * sizeof(double));"),
+    "replay_skips_last_step": ("for (int64_t t = t0; t < t1; t++) {\n                double *next",
+                               "for (int64_t t = t0; t < t1 - 1; t++) {\n                double *next"),
 }
 
 # The cheap pins: enough to kill every mutant above.
 QUICK = ("golden_n1", "golden_n2", "matrix_form", "identities", "split_sequence",
-         "torch_autograd")
+         "torch_autograd", "torch_autograd_long")
 
 
 @pytest.mark.parametrize("name", list(MUTANTS))
