@@ -35,8 +35,9 @@
  * 16-byte aligned.  Calls only enqueue work on `stream` (NULL = the default
  * stream) and return; the library never allocates, frees or synchronises.
  * Results are deterministic (fixed reduction order, no float atomics).
- * There is no global mutable state: concurrent calls on different streams
- * are safe when their output buffers do not overlap.
+ * Apart from one fault word per device (wkv7_fault_status) and the test
+ * hooks, there is no global mutable state: concurrent calls on different
+ * streams are safe when their output buffers do not overlap.
  *
  * Errors: every argument is validated before anything is enqueued; a
  * negative status means nothing was written.  WKV7_ERR_HIP reports a launch
@@ -114,14 +115,19 @@ enum {
     WKV7_OK = 0,
     WKV7_ERR_INVALID = -1,      /* NULL/misaligned pointer, negative size,
                                    bad dtype, chunk or algo, size overflow */
-    WKV7_ERR_UNSUPPORTED = -2,  /* N not in {16, 64}; CHUNKED where it does
-                                   not apply */
+    WKV7_ERR_UNSUPPORTED = -2,  /* N not in {16, 64}; CHUNKED or fused
+                                   inputs where they do not apply */
     WKV7_ERR_WORKSPACE = -3,    /* workspace missing or too small */
     WKV7_ERR_HIP = -4           /* a kernel launch failed */
 };
 
-/* Bytes of the checkpoint record for `shape`:
- * roundup(B*H*ceil(T/C)*N*N*4, 256) + B*T*H*N*4; 0 when the shape is invalid.
+/* Bytes of the checkpoint record for `shape`.  The record replaces the
+ * page's cache of every state in rx_wkv7_backward with the state at the
+ * start of every C-step chunk, from which the backward recomputes the
+ * chunk (the per-chunk start states of the burn_dragon_kernel
+ * src/sequence/rwkv8/backward.rs page, chunk_rho_start, are the prior art):
+ * roundup(B*H*ceil(T/C)*N*N*4, 256) + B*T*H*N*4 bytes; 0 when the shape
+ * is invalid.
  * Shapes of few, long sequences run split into segments (N = 64, C = 64,
  * T*H*64*4 < 2^31, B*H <= 64, at least 4 chunks; the count, up to 8, and
  * the segment length follow from the shape): their record rounds the sa
@@ -132,7 +138,8 @@ enum {
  * their outputs. */
 size_t wkv7_checkpoint_bytes(const wkv7_shape *shape);
 
-/* Bytes of device workspace wkv7_backward needs: the per-(b,h) state
+/* Bytes of device workspace wkv7_backward needs (this library's own
+ * layout; the pages have no such buffer): the per-(b,h) state
  * sub-checkpoints of one chunk and one int per (b,h) (for a split shape
  * also one int and one N x N fp32 state gradient per (b,h) and segment),
  * plus room for the checkpoint record itself when `ckpt_provided` is 0.
@@ -179,7 +186,6 @@ int wkv7_backward(const wkv7_shape *shape,
                   float *ds0, void *workspace, size_t workspace_bytes,
                   hipStream_t stream);
 
-/* Static text for a status code. */
 /* The time-mix epilogue after the scan, N = 64 (Foundry page
  * "rwkvx/rx_pretrain.c": gn_forward, the bonus term and the gate g applied
  * to the scan's output in rx_timemix_forward_seq, and the per-token
@@ -211,7 +217,37 @@ int wkv7_epilogue_backward(const wkv7_shape *shape, const float *dz, const float
                            float *dk, float *dv, float *dln_w, float *dln_b, float *dr_k,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Static text for a status code. */
 const char *wkv7_status_string(int status);
+
+/* Fault bits of the current device.  The N = 64 forward's helper waves wait
+ * for each other with a bounded poll (about 30 ms per wait; a correct build
+ * never reaches the bound).  A wait that gives up makes its workgroup
+ * overwrite every output it wrote (its y and sa-tape rows, checkpoint slots
+ * and final state) with NaN and sets bit 0 of a per-device fault word, so
+ * that no finite wrong value is returned silently.  This call waits for
+ * `stream` (the only call in the library that synchronises), stores the bits
+ * in *faults and clears them when `clear` is non-zero.  Returns WKV7_OK,
+ * WKV7_ERR_INVALID (faults NULL) or WKV7_ERR_HIP. */
+enum {
+    WKV7_FAULT_HELPER_WAIT = 1
+};
+int wkv7_fault_status(unsigned *faults, int clear, hipStream_t stream);
+
+/* Test hooks, for the library's own tests only (process-global, not
+ * thread-safe, never needed by a caller):
+ *   WKV7_HOOK_FAULT_INJECT, value 0 or 1: with 1, every workgroup of the
+ *     N = 64 forward reports a given-up helper wait (NaN outputs, fault bit)
+ *     although every wait still completes normally;
+ *   WKV7_HOOK_FAIL_LAUNCHES, value n >= 0: the next n calls that enqueue
+ *     work return WKV7_ERR_HIP as if their launch had failed (their work is
+ *     still enqueued).
+ * Returns WKV7_OK, or WKV7_ERR_INVALID for an unknown hook or value. */
+enum {
+    WKV7_HOOK_FAULT_INJECT = 1,
+    WKV7_HOOK_FAIL_LAUNCHES = 2
+};
+int wkv7_test_hook(int hook, int64_t value);
 
 /* ABI version (major * 100 + minor). */
 int wkv7_abi_version(void);

@@ -16,7 +16,11 @@ WKV7_OK, WKV7_ERR_INVALID, WKV7_ERR_UNSUPPORTED, WKV7_ERR_WORKSPACE, WKV7_ERR_HI
 # Every function the C header declares, for the symbol-export test.
 EXPORTS = ("wkv7_checkpoint_bytes", "wkv7_backward_workspace_bytes", "wkv7_forward",
            "wkv7_backward", "wkv7_epilogue_workspace_bytes", "wkv7_epilogue_forward",
-           "wkv7_epilogue_backward", "wkv7_status_string", "wkv7_abi_version")
+           "wkv7_epilogue_backward", "wkv7_status_string", "wkv7_abi_version",
+           "wkv7_fault_status", "wkv7_test_hook")
+
+WKV7_FAULT_HELPER_WAIT = 1
+WKV7_HOOK_FAULT_INJECT, WKV7_HOOK_FAIL_LAUNCHES = 1, 2
 
 
 WKV7_FUSED_INPUTS = 1   # wkv7_shape.flags bit
@@ -66,6 +70,10 @@ def lib():
     L.wkv7_status_string.restype = ctypes.c_char_p
     L.wkv7_abi_version.argtypes = []
     L.wkv7_abi_version.restype = i32
+    L.wkv7_fault_status.argtypes = [ctypes.POINTER(ctypes.c_uint), i32, vp]
+    L.wkv7_fault_status.restype = i32
+    L.wkv7_test_hook.argtypes = [i32, ctypes.c_int64]
+    L.wkv7_test_hook.restype = i32
     _LIB = L
     return L
 

@@ -22,6 +22,21 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocate the buffers a call creates on the stream its kernels run on,
+    so that the caching allocator does not hand their memory to other work
+    before those kernels are done with it."""
+    return torch.cuda.stream(stream) if stream is not None else _Nothing()
+
+
+class _Nothing:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *exc):
+        return False
+
+
 _ALGOS = {"auto": _lib.WKV7_ALGO_AUTO, "scan": _lib.WKV7_ALGO_SCAN,
           "chunked": _lib.WKV7_ALGO_CHUNKED}
 
@@ -79,13 +94,14 @@ def wkv7_forward(r, w, k, v, a, b, s0=None, *, chunk=64, want_y=True, want_sT=Tr
     _check_state("s0", s0, B, H, N)
     dev = r.device
     y, sT, ckpt = out if out is not None else (None, None, None)
-    if want_y and y is None:
-        y = torch.empty((B, T, H, N), device=dev, dtype=torch.float32)
-    if want_sT and sT is None:
-        sT = torch.empty((B, H, N, N), device=dev, dtype=torch.float32)
-    if want_ckpt and ckpt is None:
-        ckpt = torch.empty(wkv7_checkpoint_bytes(B, T, H, N, dt, chunk) // 4, device=dev,
-                           dtype=torch.float32)
+    with _on(stream):
+        if want_y and y is None:
+            y = torch.empty((B, T, H, N), device=dev, dtype=torch.float32)
+        if want_sT and sT is None:
+            sT = torch.empty((B, H, N, N), device=dev, dtype=torch.float32)
+        if want_ckpt and ckpt is None:
+            ckpt = torch.empty(wkv7_checkpoint_bytes(B, T, H, N, dt, chunk) // 4, device=dev,
+                               dtype=torch.float32)
     sh = make_shape(B, T, H, N, dt, chunk, fused=fused)
     rc = _lib.lib().wkv7_forward(ctypes.byref(sh), *map(_ptr, (r, w, k, v, a, b, s0)),
                                  _ptr(y if want_y else None), _ptr(sT if want_sT else None),
@@ -108,16 +124,17 @@ def wkv7_backward(r, w, k, v, a, b, dy, s0=None, dsT=None, ckpt=None, *, chunk=6
     dev = r.device
     names = ("dr", "dw", "dk", "dv", "da", "db")
     grads = dict(out) if out is not None else {}
-    for n in names:
-        if grads.get(n) is None:
-            grads[n] = torch.empty((B, T, H, N), device=dev, dtype=torch.float32)
-    if want_ds0 and grads.get("ds0") is None:
-        grads["ds0"] = torch.empty((B, H, N, N), device=dev, dtype=torch.float32)
+    need = wkv7_backward_workspace_bytes(B, T, H, N, dt, chunk, ckpt is not None)
+    with _on(stream):
+        for n in names:
+            if grads.get(n) is None:
+                grads[n] = torch.empty((B, T, H, N), device=dev, dtype=torch.float32)
+        if want_ds0 and grads.get("ds0") is None:
+            grads["ds0"] = torch.empty((B, H, N, N), device=dev, dtype=torch.float32)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     if not want_ds0:
         grads["ds0"] = None
-    need = wkv7_backward_workspace_bytes(B, T, H, N, dt, chunk, ckpt is not None)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     sh = make_shape(B, T, H, N, dt, chunk, algo, fused=fused)
     rc = _lib.lib().wkv7_backward(
@@ -140,7 +157,9 @@ def wkv7_epilogue_forward(y, r, k, v, g, ln_w, ln_b, r_k, *, stream=None, out=No
     _check_f32("y", y, (B, T, H, N))
     for n, p in (("ln_w", ln_w), ("ln_b", ln_b), ("r_k", r_k)):
         _check_f32(n, p, (H, N))
-    z = out if out is not None else torch.empty((B, T, H, N), device=y.device, dtype=torch.float32)
+    with _on(stream):
+        z = out if out is not None else torch.empty((B, T, H, N), device=y.device,
+                                                    dtype=torch.float32)
     sh = make_shape(B, T, H, N, dt)
     rc = _lib.lib().wkv7_epilogue_forward(ctypes.byref(sh), *map(_ptr, (y, r, k, v, g, ln_w, ln_b, r_k, z)),
                                           _stream(stream))
@@ -157,14 +176,15 @@ def wkv7_epilogue_backward(dz, y, r, k, v, g, ln_w, ln_b, r_k, *, workspace=None
     for n, p in (("ln_w", ln_w), ("ln_b", ln_b), ("r_k", r_k)):
         _check_f32(n, p, (H, N))
     dev = y.device
-    out = {n: torch.empty((B, T, H, N), device=dev, dtype=torch.float32)
-           for n in ("dy", "dg", "dr", "dk", "dv")}
-    for n in ("dln_w", "dln_b", "dr_k"):
-        out[n] = torch.empty((H, N), device=dev, dtype=torch.float32)
     sh = make_shape(B, T, H, N, dt)
     need = _lib.lib().wkv7_epilogue_workspace_bytes(ctypes.byref(sh))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    with _on(stream):
+        out = {n: torch.empty((B, T, H, N), device=dev, dtype=torch.float32)
+               for n in ("dy", "dg", "dr", "dk", "dv")}
+        for n in ("dln_w", "dln_b", "dr_k"):
+            out[n] = torch.empty((H, N), device=dev, dtype=torch.float32)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, device=dev, dtype=torch.uint8)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _lib.lib().wkv7_epilogue_backward(
         ctypes.byref(sh), *map(_ptr, (dz, y, r, k, v, g, ln_w, ln_b, r_k)),

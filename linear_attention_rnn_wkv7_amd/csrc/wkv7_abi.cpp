@@ -5,9 +5,15 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 #include "wkv7_internal.h"
 
 namespace {
+
+// Test hooks (wkv7_test_hook); zero in production.
+std::atomic<int> g_fault_inject{0};
+std::atomic<int64_t> g_fail_launches{0};
 
 constexpr size_t kAlign = 256;   // workspace sub-buffer alignment
 
@@ -161,10 +167,23 @@ size_t workspace_bytes(const Dims &d, bool ckpt_provided)
 
 int hip_status(hipError_t e)
 {
-    return e == hipSuccess ? WKV7_OK : WKV7_ERR_HIP;
+    if (e != hipSuccess) return WKV7_ERR_HIP;
+    int64_t n = g_fail_launches.load();
+    while (n > 0 && !g_fail_launches.compare_exchange_weak(n, n - 1)) {
+    }
+    return n > 0 ? WKV7_ERR_HIP : WKV7_OK;
 }
 
 }  // namespace
+
+namespace wkv7 {
+
+int test_fault_inject()
+{
+    return g_fault_inject.load();
+}
+
+}  // namespace wkv7
 
 extern "C" {
 
@@ -416,12 +435,46 @@ int wkv7_epilogue_backward(const wkv7_shape *shape, const float *dz, const float
     return hip_status(wkv7::launch_epilogue_backward(L, stream));
 }
 
+int wkv7_fault_status(unsigned *faults, int clear, hipStream_t stream)
+{
+    if (!faults) return WKV7_ERR_INVALID;
+    unsigned *word = wkv7::fault_word();
+    if (!word) return WKV7_ERR_HIP;
+    static const unsigned zero = 0;
+    unsigned host = 0;
+    if (hipMemcpyAsync(&host, word, sizeof host, hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return WKV7_ERR_HIP;
+    if (clear && hipMemcpyAsync(word, &zero, sizeof zero, hipMemcpyHostToDevice, stream) != hipSuccess)
+        return WKV7_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return WKV7_ERR_HIP;
+    *faults = host;
+    return WKV7_OK;
+}
+
+int wkv7_test_hook(int hook, int64_t value)
+{
+    switch (hook) {
+    case WKV7_HOOK_FAULT_INJECT:
+        if (value != 0 && value != 1) return WKV7_ERR_INVALID;
+        g_fault_inject.store((int)value);
+        return WKV7_OK;
+    case WKV7_HOOK_FAIL_LAUNCHES:
+        if (value < 0) return WKV7_ERR_INVALID;
+        g_fail_launches.store(value);
+        return WKV7_OK;
+    default:
+        return WKV7_ERR_INVALID;
+    }
+}
+
 const char *wkv7_status_string(int status)
 {
     switch (status) {
     case WKV7_OK: return "ok";
     case WKV7_ERR_INVALID: return "invalid argument";
-    case WKV7_ERR_UNSUPPORTED: return "unsupported head size";
+    case WKV7_ERR_UNSUPPORTED:
+        return "unsupported: head size not 16 or 64, or a requested form (chunked, fused inputs) "
+               "that does not apply to this shape";
     case WKV7_ERR_WORKSPACE: return "workspace missing or too small";
     case WKV7_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
@@ -430,7 +483,7 @@ const char *wkv7_status_string(int status)
 
 int wkv7_abi_version(void)
 {
-    return 104;
+    return 105;
 }
 
 }  // extern "C"

@@ -35,6 +35,7 @@
 // product, the rescaling pass, the plain steps).  Checkpoints must fall on
 // block starts (chunk a multiple of 32).
 
+#include <atomic>
 #include <type_traits>
 
 #include "wkv7_device.h"
@@ -116,6 +117,12 @@ struct FwdcArgs {
     // at least 64.  A unit reads its carry-in state before any y store.
     int mode, nseg, nckseg;
     float *pbuf;   // [B*H][nseg][64][64]; null when the carries live in y
+    // A helper wait that gives up (see hsync) makes the workgroup overwrite
+    // every output it wrote with NaN and set bit 0 of *fault.  inject != 0
+    // (a test hook) reports a given-up wait in every workgroup while all
+    // waits still complete normally.
+    unsigned *fault;
+    int inject;
 };
 
 // kLite: units that write no y (the split's first pass), which need
@@ -133,6 +140,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
     __shared__ int smode[2];                             // 1: block rescaled
     __shared__ int hbad[2];                              // a decay out of range
     __shared__ unsigned hcnt;                            // helper arrivals
+    __shared__ int hfault;                               // a helper wait gave up
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -194,10 +202,33 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
         return (int)(rem < kTB ? rem : kTB);
     };
 
+    // Every wave ends here once.  If a helper wait gave up, the LDS data of
+    // some block may have been read before it was complete: overwrite every
+    // output of this unit with NaN (y rows, sa tape rows, checkpoint slots,
+    // the final state or carry) and report it, so that no finite wrong
+    // value is left behind.
+    auto finish = [&]() {
+        __syncthreads();
+        if (!hfault) return;
+        const float nan = __builtin_nanf("");
+        const int64_t n = T * N;
+        if (outs && p.y)
+            for (int64_t i = tid; i < n; i += kThreads) p.y[vbase + (i >> 6) * stride + (i & 63)] = nan;
+        if (outs && p.sa)
+            for (int64_t i = tid; i < n; i += kThreads) p.sa[vbase + (i >> 6) * stride + (i & 63)] = nan;
+        if (outs && p.ckpt)
+            for (int64_t c = (tb0 + p.chunk - 1) / p.chunk; c * p.chunk < tb0 + T; ++c)
+                for (int i = tid; i < N * N; i += kThreads) p.ckpt[(bh * p.nck + c) * N * N + i] = nan;
+        if (sTu)
+            for (int i = tid; i < N * N; i += kThreads) sTu[(i >> 6) * sTld + (i & 63)] = nan;
+        if (tid == 0) __hip_atomic_fetch_or(p.fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+
     if (tid == 0) {
         smode[0] = smode[1] = 0;
         hbad[0] = hbad[1] = 0;
         hcnt = 0;
+        hfault = p.inject != 0;
     }
     if (zero_v)   // v is never staged: both slots read zeros
         for (int i = tid; i < 2 * kTB * N; i += kThreads) slot[i / (kTB * N)][vV][i % (kTB * N)] = 0.f;
@@ -367,6 +398,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
                     *reinterpret_cast<float4 *>(dst + e * sTld + c) =
                         make_float4(S[e][c], S[e][c + 1], S[e][c + 2], S[e][c + 3]);
         }
+        finish();
         return;
     }
 
@@ -388,16 +420,22 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
 
     // Wait until all helper waves have arrived here.  Every helper wave
     // runs the same sequence of waits; the poll count is bounded so that a
-    // broken sequence ends the kernel with wrong results instead of a hang.
+    // broken sequence cannot hang the kernel, and a wait that gives up is
+    // recorded (finish() then poisons this unit's outputs and reports it).
     unsigned htarget = 0;
     auto hsync = [&]() {
         htarget += kNH;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         if (lane == 0) __hip_atomic_fetch_add(&hcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        bool arrived = false;
         for (unsigned it = 0; it < kSpinMax; ++it) {
-            if (__hip_atomic_load(&hcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= htarget) break;
+            if (__hip_atomic_load(&hcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= htarget) {
+                arrived = true;
+                break;
+            }
             __builtin_amdgcn_s_sleep(1);
         }
+        if (!arrived && lane == 0) hfault = 1;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     };
 
@@ -812,6 +850,7 @@ __global__ void __launch_bounds__(kThreads) wkv7_fwdc_kernel(FwdcArgs<TIn> p)
     case 10: helper(std::integral_constant<int, 6>{}); break;
     default: helper(std::integral_constant<int, 7>{}); break;
     }
+    finish();
 }
 
 template <typename TIn, bool kFused>
@@ -832,6 +871,9 @@ hipError_t launch_fwdc_t(const FwdLaunch &a, int mode, hipStream_t stream)
     p.nseg = a.nseg;
     p.nckseg = a.nckseg;
     p.pbuf = a.pbuf;
+    p.fault = fault_word();
+    p.inject = test_fault_inject();
+    if (!p.fault) return hipErrorInvalidDevicePointer;
     const int64_t units = mode == 0 ? a.B * a.H
                         : mode == 1 ? a.B * a.H * (2 * a.nseg - 3) : a.B * a.H * a.nseg;
     if (mode == 1)
@@ -843,7 +885,26 @@ hipError_t launch_fwdc_t(const FwdLaunch &a, int mode, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Bit 0: a forward helper wait gave up somewhere on this device since the
+// word was last cleared (wkv7_fault_status).  One word per device.
+__device__ unsigned g_fault_word;
+
 }  // namespace
+
+unsigned *fault_word()
+{
+    static std::atomic<unsigned *> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    unsigned *ptr = cache[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        void *addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(g_fault_word)) != hipSuccess) return nullptr;
+        ptr = static_cast<unsigned *>(addr);
+        cache[dev].store(ptr, std::memory_order_release);
+    }
+    return ptr;
+}
 
 bool forward_chunked_supported(const FwdLaunch &a)
 {

@@ -95,4 +95,14 @@ hipError_t launch_epilogue_backward(const EpiLaunch &a, hipStream_t stream);
 // dst[i] = src ? src[i] : 0 for i < n.
 hipError_t launch_fill(float *dst, const float *src, size_t n, hipStream_t stream);
 
+// Devices per process the library keeps per-device addresses for.
+constexpr int kMaxDevices = 64;
+// The current device's fault word (wkv7_fwdc.hip): bit 0 is set when a
+// forward helper wait gave up; null when the device's address cannot be had.
+unsigned *fault_word();
+// Test hooks (wkv7_abi.cpp, wkv7_test_hook): report a given-up helper wait
+// in every forward workgroup; turn the status of the next launches into a
+// launch failure.
+int test_fault_inject();
+
 }  // namespace wkv7

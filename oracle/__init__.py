@@ -53,10 +53,17 @@ def _ptr(x):
 
 
 def default_threads():
+    """Host cores available to this process, capped by OMP_NUM_THREADS when
+    that is set (a machine shared by several jobs sets it to each job's
+    share)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = max(1, len(os.sched_getaffinity(0)))
     except AttributeError:
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return n
 
 
 def _check(shape_v, *arrs):

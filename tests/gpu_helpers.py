@@ -64,6 +64,47 @@ def gpu_pairs(out, pairs):
     return res
 
 
+def full_compare(inp, out, tau, label, oracle_fn=None, elem_budget=64 << 20, say=print):
+    """Every element of every output against the oracle, streamed over
+    blocks of one batch row and a group of heads (each block's oracle inputs
+    stay within ~elem_budget elements per tensor).  Returns {name: max|err| /
+    RMS(ref)} with max and RMS taken over the whole tensor, and the names over
+    tau.  oracle_fn(block_inputs) -> dict of fp64 outputs (oracle_run by
+    default)."""
+    oracle_fn = oracle_fn or oracle_run
+    B, T, Hh, N = inp["r"].shape
+    hg = max(1, min(Hh, elem_budget // max(1, T * N)))
+    stats = {}
+    for b in range(B):
+        for h0 in range(0, Hh, hg):
+            h1 = min(Hh, h0 + hg)
+            blk = {n: (None if x is None else
+                       (x[b:b + 1, :, h0:h1] if n in IN + ("dy",) else x[b:b + 1, h0:h1]))
+                   for n, x in inp.items()}
+            ref = oracle_fn(blk)
+            for n, r in ref.items():
+                if r is None or out.get(n) is None:
+                    continue
+                g = out[n][b:b + 1, h0:h1] if n in ("sT", "ds0") else out[n][b:b + 1, :, h0:h1]
+                g = to64(g)
+                st = stats.setdefault(n, [0.0, 0.0, 0])
+                if r.size:
+                    st[0] = max(st[0], float(np.max(np.abs(g - r))))
+                    st[1] += float(np.sum(r * r))
+                    st[2] += r.size
+            del ref
+    errs, bad = {}, []
+    for n, (mx, ss, cnt) in stats.items():
+        rms = float(np.sqrt(ss / cnt)) if cnt else 0.0
+        e = mx / max(rms, 1e-30) if cnt else 0.0
+        errs[n] = e
+        if not np.isfinite(e) or e > tau:
+            bad.append(n)
+    say(f"{label} (all {B * Hh} (b,h), blocks of {hg} heads): "
+        + " ".join(f"{n}={errs[n]:.2e}" for n in sorted(errs)))
+    return errs, bad
+
+
 def compare(got, ref, tau, names=("y", "sT") + GRADS + ("ds0",)):
     """Return {name: max|err| / RMS(ref)} and the list of names over tau."""
     errs, bad = {}, []

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.wkv7_abi_version() == 104
+    assert L.wkv7_abi_version() == 105
 
 
 def _shape(B=2, T=10, H=3, N=64, dtype=0, chunk=64, algo=0, flags=0):
@@ -196,15 +196,31 @@ def test_epilogue_validation():
     assert L.wkv7_epilogue_workspace_bytes(ctypes.byref(_shape(N=16))) == 0
 
 
-def test_status_strings():
-    for code in (0, -1, -2, -3, -4):
-        assert _lib.status_text(code)
-    assert _lib.status_text(-99) == "unknown status"
-
-
 def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 4, 1, 64)
     with pytest.raises(ValueError):
         api.wkv7_forward(x, x, x, x, x, x)
     with pytest.raises(ValueError):
         api.wkv7_backward(x, x, x, x, x, x, x)
+
+
+def test_test_hooks_validate():
+    """The test hooks reject unknown hooks and values, and reset cleanly
+    (no GPU call: they only set host-side switches)."""
+    L = _lib.lib()
+    assert L.wkv7_test_hook(99, 0) == _lib.WKV7_ERR_INVALID
+    assert L.wkv7_test_hook(_lib.WKV7_HOOK_FAULT_INJECT, 2) == _lib.WKV7_ERR_INVALID
+    assert L.wkv7_test_hook(_lib.WKV7_HOOK_FAIL_LAUNCHES, -1) == _lib.WKV7_ERR_INVALID
+    assert L.wkv7_test_hook(_lib.WKV7_HOOK_FAULT_INJECT, 0) == _lib.WKV7_OK
+    assert L.wkv7_test_hook(_lib.WKV7_HOOK_FAIL_LAUNCHES, 0) == _lib.WKV7_OK
+    assert L.wkv7_fault_status(None, 0, None) == _lib.WKV7_ERR_INVALID
+
+
+def test_status_strings():
+    """One distinct text per status; -2 names both of its causes."""
+    L = _lib.lib()
+    texts = {s: L.wkv7_status_string(s).decode() for s in (0, -1, -2, -3, -4, 7)}
+    assert texts[0] == "ok" and texts[7] == "unknown status"
+    assert "fused" in texts[-2] and "head size" in texts[-2]
+    assert len(set(texts.values())) == 6
+    assert _lib.status_text(-99) == "unknown status"
