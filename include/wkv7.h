@@ -186,6 +186,25 @@ int wkv7_backward(const wkv7_shape *shape,
                   float *ds0, void *workspace, size_t workspace_bytes,
                   hipStream_t stream);
 
+/* wkv7_backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results (bit
+ * for bit) and errors as wkv7_backward, except that the workspace is the
+ * library's own fixed device array of WKV7_NOALLOC_SCRATCH_BYTES bytes per
+ * GPU, which each GPU the library runs on holds until the process ends.  A
+ * shape whose workspace (wkv7_backward_workspace_bytes(shape, ckpt != NULL))
+ * exceeds that size returns WKV7_ERR_WORKSPACE before anything is enqueued.
+ * The call allocates and frees nothing.  Calls that overlap on one GPU (on
+ * different streams, or from different threads) share the array and race:
+ * order them on one stream. */
+#define WKV7_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int wkv7_backward_noalloc(const wkv7_shape *shape,
+                          const void *r, const void *w, const void *k, const void *v,
+                          const void *a, const void *b, const float *s0,
+                          const void *dy, const float *dsT, const float *ckpt,
+                          float *dr, float *dw, float *dk, float *dv, float *da, float *db,
+                          float *ds0, hipStream_t stream);
+
 /* The time-mix epilogue after the scan, N = 64 (Foundry page
  * "rwkvx/rx_pretrain.c": gn_forward, the bonus term and the gate g applied
  * to the scan's output in rx_timemix_forward_seq, and the per-token

@@ -17,7 +17,9 @@ WKV7_OK, WKV7_ERR_INVALID, WKV7_ERR_UNSUPPORTED, WKV7_ERR_WORKSPACE, WKV7_ERR_HI
 EXPORTS = ("wkv7_checkpoint_bytes", "wkv7_backward_workspace_bytes", "wkv7_forward",
            "wkv7_backward", "wkv7_epilogue_workspace_bytes", "wkv7_epilogue_forward",
            "wkv7_epilogue_backward", "wkv7_status_string", "wkv7_abi_version",
-           "wkv7_fault_status", "wkv7_test_hook")
+           "wkv7_fault_status", "wkv7_test_hook", "wkv7_backward_noalloc")
+
+WKV7_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 WKV7_FAULT_HELPER_WAIT = 1
 WKV7_HOOK_FAULT_INJECT, WKV7_HOOK_FAIL_LAUNCHES = 1, 2
@@ -60,6 +62,8 @@ def lib():
     L.wkv7_forward.restype = i32
     L.wkv7_backward.argtypes = [sp] + [vp] * 17 + [vp, sz, vp]
     L.wkv7_backward.restype = i32
+    L.wkv7_backward_noalloc.argtypes = [sp] + [vp] * 17 + [vp]
+    L.wkv7_backward_noalloc.restype = i32
     L.wkv7_epilogue_workspace_bytes.argtypes = [sp]
     L.wkv7_epilogue_workspace_bytes.restype = sz
     L.wkv7_epilogue_forward.argtypes = [sp] + [vp] * 9 + [vp]

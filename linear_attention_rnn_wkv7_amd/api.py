@@ -145,6 +145,28 @@ def wkv7_backward(r, w, k, v, a, b, dy, s0=None, dsT=None, ckpt=None, *, chunk=6
     return grads
 
 
+def wkv7_backward_noalloc(r, w, k, v, a, b, dy, s0=None, dsT=None, ckpt=None, *, out,
+                          chunk=64, stream=None, algo="auto", fused=False):
+    """wkv7_backward with the library's own fixed device workspace
+    (WKV7_NOALLOC_SCRATCH_BYTES per GPU) instead of a caller workspace; the
+    caller supplies every output in `out` (dict dr, dw, dk, dv, da, db and
+    optionally ds0), so nothing is allocated.  Returns `out`."""
+    (B, T, H, N), dt = _check_vecs("rwkvab dy", (r, w, k, v, a, b, dy))
+    _check_state("s0", s0, B, H, N)
+    _check_state("dsT", dsT, B, H, N)
+    names = ("dr", "dw", "dk", "dv", "da", "db")
+    for n in names:
+        _check_f32(n, out[n], (B, T, H, N))
+    if out.get("ds0") is not None:
+        _check_f32("ds0", out["ds0"], (B, H, N, N))
+    sh = make_shape(B, T, H, N, dt, chunk, algo, fused=fused)
+    rc = _lib.lib().wkv7_backward_noalloc(
+        ctypes.byref(sh), *map(_ptr, (r, w, k, v, a, b, s0, dy, dsT, ckpt)),
+        *map(_ptr, (out[n] for n in names)), _ptr(out.get("ds0")), _stream(stream))
+    _lib.check("wkv7_backward_noalloc", rc)
+    return out
+
+
 def _check_f32(name, t, shape):
     if t.shape != shape or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous fp32 device tensor {list(shape)}")

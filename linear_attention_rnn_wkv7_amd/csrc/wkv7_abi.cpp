@@ -183,6 +183,104 @@ int test_fault_inject()
     return g_fault_inject.load();
 }
 
+int backward_entry(const wkv7_shape *shape, const void *r, const void *w, const void *k,
+                   const void *v, const void *a, const void *b, const float *s0,
+                   const void *dy, const float *dsT, const float *ckpt,
+                   float *dr, float *dw, float *dk, float *dv, float *da, float *db,
+                   float *ds0, void *workspace, size_t workspace_bytes_given,
+                   int (*scratch)(size_t need, void **ptr), hipStream_t stream)
+{
+    Dims d;
+    int rc = check_shape(shape, &d);
+    if (rc != WKV7_OK) return rc;
+    if (d.B * d.H == 0) return WKV7_OK;
+    const void *in[7] = {r, w, k, v, a, b, dy};
+    float *grad[6] = {dr, dw, dk, dv, da, db};
+    for (const void *p : in) {
+        if (d.T > 0 && !p) return WKV7_ERR_INVALID;
+        if (!aligned(p)) return WKV7_ERR_INVALID;
+    }
+    for (float *p : grad) {
+        if (d.T > 0 && !p) return WKV7_ERR_INVALID;
+        if (!aligned(p)) return WKV7_ERR_INVALID;
+    }
+    for (const void *p : {(const void *)s0, (const void *)dsT, (const void *)ckpt,
+                          (const void *)ds0})
+        if (!aligned(p)) return WKV7_ERR_INVALID;
+
+    if (d.algo == WKV7_ALGO_CHUNKED &&
+        !(d.N == 64 && d.C == 64 && (d.T == 0 || wkv7::chunk_offsets_fit(d.T, d.H))))
+        return WKV7_ERR_UNSUPPORTED;
+    if (d.fused && !fused_supported(d)) return WKV7_ERR_UNSUPPORTED;
+    if (d.T == 0) {
+        if (!ds0) return WKV7_OK;
+        return hip_status(wkv7::launch_fill(ds0, dsT, d.state_elems, stream));
+    }
+    const size_t need = workspace_bytes(d, ckpt != nullptr);
+    if (scratch) {   // no caller workspace: the library's own scratch
+        rc = scratch(need, &workspace);
+        if (rc != WKV7_OK) return rc;
+        workspace_bytes_given = need;
+    }
+    if (need > 0 && (!workspace || workspace_bytes_given < need)) return WKV7_ERR_WORKSPACE;
+    if (((uintptr_t)workspace % kAlign) != 0) return WKV7_ERR_WORKSPACE;
+
+    char *ws = static_cast<char *>(workspace);
+    float *sub = reinterpret_cast<float *>(ws);
+    const float *ck = ckpt;
+    if (!ckpt) {
+        float *own = reinterpret_cast<float *>(ws + sub_region(d) + flag_region(d) + split_region(d));
+        wkv7::FwdLaunch F;
+        for (int i = 0; i < 6; ++i) F.in[i] = in[i];
+        F.s0 = s0;
+        F.y = nullptr;
+        F.sT = nullptr;
+        F.ckpt = own;
+        F.satape = const_cast<float *>(tape_of(own, d));
+        F.B = d.B;
+        F.T = d.T;
+        F.H = d.H;
+        F.N = d.N;
+        F.dtype = d.dtype;
+        F.chunk = (int)d.C;
+        F.fused = d.fused;
+        if (d.nseg > 1) {
+            F.nseg = d.nseg;
+            F.nckseg = d.nckseg;
+            F.pbuf = pbuf_of(own, d);
+        }
+        rc = hip_status(wkv7::launch_forward(F, stream));
+        if (rc != WKV7_OK) return rc;
+        ck = own;
+    }
+    wkv7::BwdLaunch L;
+    for (int i = 0; i < 7; ++i) L.in[i] = in[i];
+    L.ckpt = ck;
+    L.satape = tape_of(ck, d);
+    L.dsT = dsT;
+    for (int i = 0; i < 6; ++i) L.grad[i] = grad[i];
+    L.ds0 = ds0;
+    L.sub = sub;
+    L.flags = reinterpret_cast<int *>(ws + sub_region(d));
+    L.B = d.B;
+    L.T = d.T;
+    L.H = d.H;
+    L.N = d.N;
+    L.dtype = d.dtype;
+    L.chunk = (int)d.C;
+    L.algo = d.algo;
+    L.fused = d.fused;
+    if (d.nseg > 1) {
+        char *sp = ws + sub_region(d) + flag_region(d);
+        L.nseg = d.nseg;
+        L.nckseg = d.nckseg;
+        L.pbuf = pbuf_of(ck, d);
+        L.unit_flags = reinterpret_cast<int *>(sp);
+        L.gbuf = reinterpret_cast<float *>(sp + round_up((size_t)(d.B * d.H) * d.nseg * sizeof(int)));
+    }
+    return hip_status(wkv7::launch_backward(L, stream));
+}
+
 }  // namespace wkv7
 
 extern "C" {
@@ -260,90 +358,8 @@ int wkv7_backward(const wkv7_shape *shape, const void *r, const void *w, const v
                   float *ds0, void *workspace, size_t workspace_bytes_given,
                   hipStream_t stream)
 {
-    Dims d;
-    int rc = check_shape(shape, &d);
-    if (rc != WKV7_OK) return rc;
-    if (d.B * d.H == 0) return WKV7_OK;
-    const void *in[7] = {r, w, k, v, a, b, dy};
-    float *grad[6] = {dr, dw, dk, dv, da, db};
-    for (const void *p : in) {
-        if (d.T > 0 && !p) return WKV7_ERR_INVALID;
-        if (!aligned(p)) return WKV7_ERR_INVALID;
-    }
-    for (float *p : grad) {
-        if (d.T > 0 && !p) return WKV7_ERR_INVALID;
-        if (!aligned(p)) return WKV7_ERR_INVALID;
-    }
-    for (const void *p : {(const void *)s0, (const void *)dsT, (const void *)ckpt,
-                          (const void *)ds0})
-        if (!aligned(p)) return WKV7_ERR_INVALID;
-
-    if (d.algo == WKV7_ALGO_CHUNKED &&
-        !(d.N == 64 && d.C == 64 && (d.T == 0 || wkv7::chunk_offsets_fit(d.T, d.H))))
-        return WKV7_ERR_UNSUPPORTED;
-    if (d.fused && !fused_supported(d)) return WKV7_ERR_UNSUPPORTED;
-    if (d.T == 0) {
-        if (!ds0) return WKV7_OK;
-        return hip_status(wkv7::launch_fill(ds0, dsT, d.state_elems, stream));
-    }
-    const size_t need = workspace_bytes(d, ckpt != nullptr);
-    if (need > 0 && (!workspace || workspace_bytes_given < need)) return WKV7_ERR_WORKSPACE;
-    if (((uintptr_t)workspace % kAlign) != 0) return WKV7_ERR_WORKSPACE;
-
-    char *ws = static_cast<char *>(workspace);
-    float *sub = reinterpret_cast<float *>(ws);
-    const float *ck = ckpt;
-    if (!ckpt) {
-        float *own = reinterpret_cast<float *>(ws + sub_region(d) + flag_region(d) + split_region(d));
-        wkv7::FwdLaunch F;
-        for (int i = 0; i < 6; ++i) F.in[i] = in[i];
-        F.s0 = s0;
-        F.y = nullptr;
-        F.sT = nullptr;
-        F.ckpt = own;
-        F.satape = const_cast<float *>(tape_of(own, d));
-        F.B = d.B;
-        F.T = d.T;
-        F.H = d.H;
-        F.N = d.N;
-        F.dtype = d.dtype;
-        F.chunk = (int)d.C;
-        F.fused = d.fused;
-        if (d.nseg > 1) {
-            F.nseg = d.nseg;
-            F.nckseg = d.nckseg;
-            F.pbuf = pbuf_of(own, d);
-        }
-        rc = hip_status(wkv7::launch_forward(F, stream));
-        if (rc != WKV7_OK) return rc;
-        ck = own;
-    }
-    wkv7::BwdLaunch L;
-    for (int i = 0; i < 7; ++i) L.in[i] = in[i];
-    L.ckpt = ck;
-    L.satape = tape_of(ck, d);
-    L.dsT = dsT;
-    for (int i = 0; i < 6; ++i) L.grad[i] = grad[i];
-    L.ds0 = ds0;
-    L.sub = sub;
-    L.flags = reinterpret_cast<int *>(ws + sub_region(d));
-    L.B = d.B;
-    L.T = d.T;
-    L.H = d.H;
-    L.N = d.N;
-    L.dtype = d.dtype;
-    L.chunk = (int)d.C;
-    L.algo = d.algo;
-    L.fused = d.fused;
-    if (d.nseg > 1) {
-        char *sp = ws + sub_region(d) + flag_region(d);
-        L.nseg = d.nseg;
-        L.nckseg = d.nckseg;
-        L.pbuf = pbuf_of(ck, d);
-        L.unit_flags = reinterpret_cast<int *>(sp);
-        L.gbuf = reinterpret_cast<float *>(sp + round_up((size_t)(d.B * d.H) * d.nseg * sizeof(int)));
-    }
-    return hip_status(wkv7::launch_backward(L, stream));
+    return wkv7::backward_entry(shape, r, w, k, v, a, b, s0, dy, dsT, ckpt, dr, dw, dk, dv, da, db,
+                                ds0, workspace, workspace_bytes_given, nullptr, stream);
 }
 
 size_t wkv7_epilogue_workspace_bytes(const wkv7_shape *shape)

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "wkv7.h"
+
 namespace wkv7 {
 
 // Sub-chunk length of the backward's in-register recompute.
@@ -104,5 +106,15 @@ unsigned *fault_word();
 // in every forward workgroup; turn the status of the next launches into a
 // launch failure.
 int test_fault_inject();
+
+// The body of wkv7_backward.  With `scratch` non-null the workspace
+// arguments are ignored: after validation, scratch(need, &ptr) supplies
+// `need` bytes of device workspace (or returns an error status).
+int backward_entry(const wkv7_shape *shape, const void *r, const void *w, const void *k,
+                   const void *v, const void *a, const void *b, const float *s0,
+                   const void *dy, const float *dsT, const float *ckpt,
+                   float *dr, float *dw, float *dk, float *dv, float *da, float *db,
+                   float *ds0, void *workspace, size_t workspace_bytes,
+                   int (*scratch)(size_t need, void **ptr), hipStream_t stream);
 
 }  // namespace wkv7

@@ -224,3 +224,17 @@ def test_status_strings():
     assert "fused" in texts[-2] and "head size" in texts[-2]
     assert len(set(texts.values())) == 6
     assert _lib.status_text(-99) == "unknown status"
+
+
+def test_noalloc_rejects_oversized_shape_before_launch():
+    """wkv7_backward_noalloc refuses a shape whose workspace exceeds its
+    fixed array with WKV7_ERR_WORKSPACE, before touching any pointer."""
+    B, T, Hh = 16, 4096, 256
+    sh = _shape(B=B, T=T, H=Hh)
+    assert _lib.lib().wkv7_backward_workspace_bytes(ctypes.byref(sh), 1) > \
+        _lib.WKV7_NOALLOC_SCRATCH_BYTES
+    p = [ctypes.c_void_p(FAKE)] * 17
+    p[6] = p[8] = p[16] = None
+    assert _lib.lib().wkv7_backward_noalloc(ctypes.byref(sh), *p, None) == _lib.WKV7_ERR_WORKSPACE
+    p[0] = None   # validation still comes first
+    assert _lib.lib().wkv7_backward_noalloc(ctypes.byref(sh), *p, None) == _lib.WKV7_ERR_INVALID
