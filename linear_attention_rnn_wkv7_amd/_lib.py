@@ -18,6 +18,10 @@ EXPORTS = ("wkv7_checkpoint_bytes", "wkv7_backward_workspace_bytes", "wkv7_forwa
            "wkv7_backward", "wkv7_epilogue_workspace_bytes", "wkv7_epilogue_forward",
            "wkv7_epilogue_backward", "wkv7_status_string", "wkv7_abi_version",
            "wkv7_fault_status", "wkv7_test_hook", "wkv7_backward_noalloc")
+# ... and every function include/rwkv8.h declares
+RWKV8_EXPORTS = ("rwkv8_checkpoint_bytes", "rwkv8_backward_workspace_bytes", "rwkv8_forward",
+                 "rwkv8_backward")
+WKV7_FAULT_RWKV8_DECAY = 2
 
 WKV7_NOALLOC_SCRATCH_BYTES = 128 << 20
 
@@ -32,6 +36,11 @@ class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("N", ctypes.c_int64), ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("algo", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class Rwkv8Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("Hv", ctypes.c_int64), ("L", ctypes.c_int64), ("E", ctypes.c_int64)]
 
 
 class Wkv7Error(RuntimeError):
@@ -78,6 +87,15 @@ def lib():
     L.wkv7_fault_status.restype = i32
     L.wkv7_test_hook.argtypes = [i32, ctypes.c_int64]
     L.wkv7_test_hook.restype = i32
+    s8 = ctypes.POINTER(Rwkv8Shape)
+    L.rwkv8_checkpoint_bytes.argtypes = [s8]
+    L.rwkv8_checkpoint_bytes.restype = sz
+    L.rwkv8_backward_workspace_bytes.argtypes = [s8, i32]
+    L.rwkv8_backward_workspace_bytes.restype = sz
+    L.rwkv8_forward.argtypes = [s8] + [vp] * 9 + [vp]
+    L.rwkv8_forward.restype = i32
+    L.rwkv8_backward.argtypes = [s8] + [vp] * 14 + [vp, sz, vp]
+    L.rwkv8_backward.restype = i32
     _LIB = L
     return L
 

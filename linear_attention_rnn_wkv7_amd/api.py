@@ -214,3 +214,87 @@ def wkv7_epilogue_backward(dz, y, r, k, v, g, ln_w, ln_b, r_k, *, workspace=None
         _ptr(workspace), ws_bytes, _stream(stream))
     _lib.check("wkv7_epilogue_backward", rc)
     return out
+
+
+# ---------------------------------------------------------------- RWKV-8 rho
+
+def _rwkv8_dims(q, v, decay):
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [B, H, T, L] and v [B, Hv, T, E]")
+    B, H, T, L = q.shape
+    Bv, Hv, Tv, E = v.shape
+    if Bv != B or Tv != T or Hv not in (1, H) or tuple(decay.shape) != (H, L):
+        raise ValueError(f"shapes q {tuple(q.shape)} v {tuple(v.shape)} decay {tuple(decay.shape)}")
+    for n, t in (("q", q), ("v", v), ("decay", decay)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous fp32 device tensor")
+    return B, H, T, L, Hv, E
+
+
+def rwkv8_shape(B, T, H, Hv, L=64, E=64):
+    return _lib.Rwkv8Shape(B, T, H, Hv, L, E)
+
+
+def rwkv8_checkpoint_bytes(B, T, H, Hv, L=64, E=64):
+    return _lib.lib().rwkv8_checkpoint_bytes(ctypes.byref(rwkv8_shape(B, T, H, Hv, L, E)))
+
+
+def rwkv8_backward_workspace_bytes(B, T, H, Hv, L=64, E=64, ckpt_provided=True):
+    return _lib.lib().rwkv8_backward_workspace_bytes(ctypes.byref(rwkv8_shape(B, T, H, Hv, L, E)),
+                                                      int(bool(ckpt_provided)))
+
+
+def rwkv8_forward(q, v, decay, rho0=None, norm0=None, *, want_y=True, want_state=True,
+                  want_ckpt=False, stream=None, out=None):
+    """The RWKV-8 rho / rho_norm forward (rwkv8_forward).  q [B, H, T, 64],
+    v [B, Hv, T, 64], decay [H, 64], rho0 [B, H, 64, 64], norm0 [B, H, 64].
+    Returns (y, rhoT, normT, ckpt); unwanted outputs are None."""
+    B, H, T, L, Hv, E = _rwkv8_dims(q, v, decay)
+    dev = q.device
+    y, rT, nT, ck = out if out is not None else (None, None, None, None)
+    with _on(stream):
+        if want_y and y is None:
+            y = torch.empty((B, H, T, E), device=dev, dtype=torch.float32)
+        if want_state and rT is None:
+            rT = torch.empty((B, H, L, E), device=dev, dtype=torch.float32)
+            nT = torch.empty((B, H, L), device=dev, dtype=torch.float32)
+        if want_ckpt and ck is None:
+            ck = torch.empty(rwkv8_checkpoint_bytes(B, T, H, Hv, L, E) // 4, device=dev,
+                             dtype=torch.float32)
+    sh = rwkv8_shape(B, T, H, Hv, L, E)
+    rc = _lib.lib().rwkv8_forward(ctypes.byref(sh), *map(_ptr, (q, v, decay, rho0, norm0)),
+                                  _ptr(y if want_y else None), _ptr(rT if want_state else None),
+                                  _ptr(nT if want_state else None), _ptr(ck if want_ckpt else None),
+                                  _stream(stream))
+    _lib.check("rwkv8_forward", rc)
+    return ((y if want_y else None), (rT if want_state else None), (nT if want_state else None),
+            (ck if want_ckpt else None))
+
+
+def rwkv8_backward(q, v, decay, dy, rho0=None, norm0=None, drhoT=None, dnormT=None, ckpt=None, *,
+                   want_state_grads=True, workspace=None, stream=None, out=None):
+    """The RWKV-8 rho / rho_norm backward (rwkv8_backward).  Returns dict dq,
+    dv, ddecay, drho0, dnorm0 (the last two None when not wanted)."""
+    B, H, T, L, Hv, E = _rwkv8_dims(q, v, decay)
+    dev = q.device
+    g = dict(out) if out is not None else {}
+    need = rwkv8_backward_workspace_bytes(B, T, H, Hv, L, E, ckpt is not None)
+    with _on(stream):
+        shapes = {"dq": (B, H, T, L), "dv": (B, Hv, T, E), "ddecay": (H, L)}
+        if want_state_grads:
+            shapes.update(drho0=(B, H, L, E), dnorm0=(B, H, L))
+        for n, shp in shapes.items():
+            if g.get(n) is None:
+                g[n] = torch.empty(shp, device=dev, dtype=torch.float32)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    if not want_state_grads:
+        g["drho0"] = g["dnorm0"] = None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sh = rwkv8_shape(B, T, H, Hv, L, E)
+    rc = _lib.lib().rwkv8_backward(
+        ctypes.byref(sh), *map(_ptr, (q, v, decay, rho0, norm0, dy, drhoT, dnormT, ckpt)),
+        *map(_ptr, (g["dq"], g["dv"], g["ddecay"], g["drho0"], g["dnorm0"])),
+        _ptr(workspace), ws_bytes, _stream(stream))
+    _lib.check("rwkv8_backward", rc)
+    return g

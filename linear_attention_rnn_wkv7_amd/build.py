@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libwkv7.so")
 OBJDIR = os.path.join(ROOT, "_build")
 SOURCES = ["wkv7_abi.cpp", "wkv7_fwd.hip", "wkv7_bwd.hip", "wkv7_bwdc.hip", "wkv7_fwdc.hip",
            "wkv7_decode.hip", "wkv7_split.hip",
-           "wkv7_epilogue.hip", "wkv7_noalloc.hip"]
+           "wkv7_epilogue.hip", "wkv7_noalloc.hip", "rwkv8.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU forms are switched off for the device code.

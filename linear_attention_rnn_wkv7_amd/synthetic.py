@@ -114,3 +114,74 @@ def vec_slice(x, b, h):
 def state_slice(x, b, h):
     """The [1, 1, N, N] slice of (b, h) from a [B, H, N, N] state tensor."""
     return None if x is None else x[b:b + 1, h:h + 1]
+
+
+# ------------------------------------------------ RWKV-8 rho / rho_norm inputs
+#   q = relu(N(0, 1))         non-negative latent features, half of them zero
+#   v, dy ~ N(0, 1)
+#   decay = exp(-c sigmoid(x)), x ~ N(0, 1), per (head, latent)   (in (0.545, 1))
+#   carry-in: norm0 ~ U(0.5, 2.5), rho0 = norm0 * N(0, 1) per element (a
+#             state whose rows are norm-weighted averages of values)
+#   final-state gradients (when the workload has them): N(0, 1)
+# Draw order from one generator: q, v, x, dy, norm0, rho0, drhoT, dnormT.
+
+@dataclass(frozen=True)
+class Rwkv8Workload:
+    name: str
+    B: int
+    T: int
+    H: int
+    Hv: int
+    has_state: bool
+    has_final_grads: bool
+    seed: int
+    L: int = 64
+    E: int = 64
+
+    @property
+    def tokens(self):
+        return self.B * self.T
+
+
+RWKV8_WORKLOADS = {
+    w.name: w
+    for w in (
+        Rwkv8Workload("rwkv8_b2_t300_h4", 2, 300, 4, 4, True, True, 2001),
+        # the WKV7 benchmark's shape (width 2048 as 32 heads of 64) with a
+        # carry-in state
+        Rwkv8Workload("rwkv8_b8_t4096_h32", 8, 4096, 32, 32, True, False, 2002),
+    )
+}
+
+
+def rwkv8_custom(B, T, H, Hv=None, has_state=True, has_final_grads=True, seed=7):
+    Hv = H if Hv is None else Hv
+    return Rwkv8Workload(f"rwkv8_custom_b{B}_t{T}_h{H}_hv{Hv}", B, T, H, Hv, has_state,
+                         has_final_grads, seed)
+
+
+def make_rwkv8_inputs(wl: Rwkv8Workload, device="cpu", seed: Optional[int] = None):
+    """Dict of fp32 tensors q, v, decay, dy, rho0, norm0, drhoT, dnormT (the
+    last four None when the workload has no carry-in state / final-state
+    gradients)."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed if seed is None else seed)
+    f32 = torch.float32
+
+    def randn(shape):
+        return torch.randn(shape, generator=g, device=dev, dtype=f32)
+
+    q = torch.relu(randn((wl.B, wl.H, wl.T, wl.L)))
+    v = randn((wl.B, wl.Hv, wl.T, wl.E))
+    decay = torch.exp(-DECAY_COEFF * torch.sigmoid(randn((wl.H, wl.L))))
+    dy = randn((wl.B, wl.H, wl.T, wl.E))
+    out = dict(q=q, v=v, decay=decay, dy=dy, rho0=None, norm0=None, drhoT=None, dnormT=None)
+    if wl.has_state:
+        norm0 = 0.5 + 2.0 * torch.rand((wl.B, wl.H, wl.L), generator=g, device=dev, dtype=f32)
+        out["norm0"] = norm0
+        out["rho0"] = norm0[..., None] * randn((wl.B, wl.H, wl.L, wl.E))
+    if wl.has_final_grads:
+        out["drhoT"] = randn((wl.B, wl.H, wl.L, wl.E))
+        out["dnormT"] = randn((wl.B, wl.H, wl.L))
+    return out

@@ -14,16 +14,20 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "wkv7.h")
 
 
-def _declared():
-    src = open(HEADER).read()
+def _declared(header=HEADER, prefix="wkv7"):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return set(re.findall(r"\b(wkv7_[a-z_0-9]+)\s*\(", src))
+    return set(re.findall(r"\b(" + prefix + r"_[a-z_0-9]+)\s*\(", src))
 
 
 def test_exports_every_declared_symbol():
     L = _lib.lib()
     declared = _declared()
     assert declared == set(_lib.EXPORTS)
+    declared8 = _declared(os.path.join(ROOT, "include", "rwkv8.h"), "rwkv8")
+    assert declared8 == set(_lib.RWKV8_EXPORTS)
+    for name in declared8:
+        assert hasattr(L, name), name
     for name in declared:
         assert hasattr(L, name), name
     assert L.wkv7_abi_version() == 105
@@ -238,3 +242,35 @@ def test_noalloc_rejects_oversized_shape_before_launch():
     assert _lib.lib().wkv7_backward_noalloc(ctypes.byref(sh), *p, None) == _lib.WKV7_ERR_WORKSPACE
     p[0] = None   # validation still comes first
     assert _lib.lib().wkv7_backward_noalloc(ctypes.byref(sh), *p, None) == _lib.WKV7_ERR_INVALID
+
+
+
+def test_rwkv8_validation():
+    """rwkv8_* reject bad shapes and pointers before enqueuing anything."""
+    L = _lib.lib()
+    fake = ctypes.c_void_p(FAKE)
+
+    def fwd(sh, ptrs=None):
+        p = [fake] * 3 if ptrs is None else ptrs
+        return L.rwkv8_forward(ctypes.byref(sh) if sh is not None else None, *p,
+                               None, None, None, None, None, None, None)
+    sh = api.rwkv8_shape
+    assert fwd(None) == _lib.WKV7_ERR_INVALID
+    assert fwd(sh(2, 10, 3, 2)) == _lib.WKV7_ERR_INVALID          # Hv neither 1 nor H
+    assert fwd(sh(2, 10, 3, 3, 32, 64)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert fwd(sh(2, 10, 3, 3, 64, 128)) == _lib.WKV7_ERR_UNSUPPORTED
+    assert fwd(sh(-1, 10, 3, 3)) == _lib.WKV7_ERR_INVALID
+    assert fwd(sh(2, 10, 3, 3), [fake, None, fake]) == _lib.WKV7_ERR_INVALID
+    assert fwd(sh(2, 10, 3, 3), [fake, ctypes.c_void_p(FAKE + 4), fake]) == _lib.WKV7_ERR_INVALID
+    assert fwd(sh(0, 10, 3, 3), [None] * 3) == _lib.WKV7_OK
+    # sizes
+    assert L.rwkv8_checkpoint_bytes(ctypes.byref(sh(2, 130, 3, 3))) == 2 * 3 * 3 * (64 * 64 + 64) * 4
+    base = (2 * 3 * 64 * 4 + 255) // 256 * 256
+    assert L.rwkv8_backward_workspace_bytes(ctypes.byref(sh(2, 130, 3, 3)), 1) == base
+    assert L.rwkv8_backward_workspace_bytes(ctypes.byref(sh(2, 130, 3, 1)), 1) == \
+        base + (2 * 3 * 130 * 64 * 4 + 255) // 256 * 256
+    # the backward refuses a missing or small workspace
+    p = [fake] * 14
+    p[3] = p[4] = p[6] = p[7] = p[8] = p[12] = p[13] = None
+    assert L.rwkv8_backward(ctypes.byref(sh(2, 130, 3, 3)), *p, None, 0, None) == \
+        _lib.WKV7_ERR_WORKSPACE
