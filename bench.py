@@ -129,6 +129,7 @@ def decode_bench(args, wl):
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM,
             "traffic": measured_traffic("wkv7_decode_kernel", wl.name),
+            "achieved_gbps": counter_fields("wkv7_decode_kernel", wl.name, ms)["achieved_gbps"],
         },
     }
     if args.copy_bytes > 0:
@@ -275,10 +276,138 @@ def epilogue_bench(args, wl):
     print(json.dumps(rec), flush=True)
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs,
-    or None when absent or taken on a different kernel source."""
-    path = os.path.join(PROFILES, f"{kernel.replace('_kernel', '')}_{workload}_traffic.json")
+RWKV8_METRIC = "RWKV-8 rho fwd+bwd tokens/sec at 1 GPU; % of fp32 roofline (rocprof)"
+
+
+def rwkv8_algorithmic(wl):
+    """Algorithmic work per launch of the RWKV-8 rho recurrence (fp32 flops
+    with FMA = 2, HBM bytes), L = E = 64, per token-head:
+      forward : readout R^T c 2LE, state update diag(d) R + q v^T 3LE        = 5LE
+      backward: dv, dq, the decay's row sums, the carry's decay 1LE, R dy,
+                c dy^T (2LE each), the state replayed from a checkpoint 3LE  = 14LE
+      bytes   : forward q, v in, y out, a checkpoint of R and n every 64
+                steps out; backward q, v, dy and the checkpoint in, dq, dv out."""
+    th = wl.B * wl.T * wl.H
+    L, E = wl.L, wl.E
+    ck = 4.0 * (L * E + L) / 64
+    fwd_flops, bwd_flops = 5 * L * E * th, 14 * L * E * th
+    vb = 4 * E * (wl.Hv / wl.H)
+    fwd_bytes = (4 * L + vb + 4 * E + ck) * th
+    bwd_bytes = (4 * L + vb + 4 * E + ck + 4 * L + vb) * th
+    return fwd_flops, bwd_flops, fwd_bytes, bwd_bytes
+
+
+def rwkv8_bench(args, wl):
+    import numpy as np
+    import torch
+
+    import oracle.rwkv8 as R8
+    from linear_attention_rnn_wkv7_amd import api
+    from linear_attention_rnn_wkv7_amd.synthetic import make_rwkv8_inputs
+
+    inp = make_rwkv8_inputs(wl, device="cuda")
+    B, T, H, Hv, L, E = wl.B, wl.T, wl.H, wl.Hv, wl.L, wl.E
+    f32 = torch.float32
+    y = torch.empty((B, H, T, E), device="cuda", dtype=f32)
+    rT = torch.empty((B, H, L, E), device="cuda", dtype=f32)
+    nT = torch.empty((B, H, L), device="cuda", dtype=f32)
+    ck = torch.empty(api.rwkv8_checkpoint_bytes(B, T, H, Hv, L, E) // 4, device="cuda", dtype=f32)
+    grads = {"dq": torch.empty((B, H, T, L), device="cuda", dtype=f32),
+             "dv": torch.empty((B, Hv, T, E), device="cuda", dtype=f32),
+             "ddecay": torch.empty((H, L), device="cuda", dtype=f32),
+             "drho0": torch.empty((B, H, L, E), device="cuda", dtype=f32),
+             "dnorm0": torch.empty((B, H, L), device="cuda", dtype=f32)}
+    ws = torch.empty(max(1, api.rwkv8_backward_workspace_bytes(B, T, H, Hv, L, E, True)),
+                     device="cuda", dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    a = (inp["q"], inp["v"], inp["decay"])
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        api.rwkv8_forward(*a, inp["rho0"], inp["norm0"], want_ckpt=True, out=(y, rT, nT, ck),
+                          stream=stream)
+        if ev:
+            ev[1].record(stream)
+        api.rwkv8_backward(*a, inp["dy"], inp["rho0"], inp["norm0"], inp["drhoT"], inp["dnormT"],
+                           ck, workspace=ws, out=grads, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    for n, x in list(grads.items()) + [("y", y), ("rhoT", rT)]:
+        if not torch.isfinite(x).all():
+            raise RuntimeError(f"non-finite values in {n}")
+    ff, bf, fb, bb = rwkv8_algorithmic(wl)
+    t_roof = max((ff + bf) / PEAK_FP32_VALU, (fb + bb) / PEAK_HBM)
+    achieved = bf / (bwd_ms * 1e-3)
+    rec = {
+        "metric": RWKV8_METRIC, "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "Hv": Hv, "L": L, "E": E,
+                   "carry_in_state": wl.has_state},
+        "roofline": {"kernel": "rwkv8_bwd_kernel", "bound": "mfma", "achieved": achieved / 1e12,
+                     "peak": PEAK_FP32_VALU / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP32_VALU,
+                     "traffic": measured_traffic("rwkv8_bwd_kernel", wl.name),
+                     "mfma_type": "v_mfma_f32_16x16x4f32",
+                     **counter_fields("rwkv8_bwd_kernel", wl.name, bwd_ms)},
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        "fwd_bwd_roofline_frac": t_roof / (ms * 1e-3),
+    }
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, device="cuda", dtype=torch.uint8)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_bytes"] = args.copy_bytes
+    if not args.no_cpu_baseline:
+        cores = oracle_threads()
+        host = {n: (None if x is None else x.detach().cpu().double().numpy())
+                for n, x in inp.items()}
+        # whole (b, h) recurrences of the first batch rows, as many heads as
+        # fit the budget (a probe of one head sets the count)
+        def run(nb, nh):
+            sl = {n: (None if x is None else x[:nb, :nh]) for n, x in host.items()
+                  if n not in ("decay",)}
+            t0 = time.perf_counter()
+            R8.forward(sl["q"], sl["v"], host["decay"][:nh], sl["rho0"], sl["norm0"], threads=cores)
+            R8.backward(sl["q"], sl["v"], host["decay"][:nh], sl["dy"], sl["rho0"], sl["norm0"],
+                        sl["drhoT"], sl["dnormT"], threads=cores)
+            return time.perf_counter() - t0
+        probe = run(1, 1)
+        nh = int(max(1, min(H, cores * max(1, int(args.cpu_budget / max(probe, 1e-3) / 2)))))
+        el = run(1, nh)
+        rec["cpu_baseline"] = {"value": nh * T / el / H, "unit": "tokens/s", "cores": min(cores, nh),
+                               "kind": "oracle",
+                               "sample": f"{nh} of {B * H} whole (b,h) recurrences (T={T}), fp64 "
+                                         f"fwd+bwd in {el:.1f} s; tokens/s = token-heads/s / H"}
+    print(json.dumps(rec), flush=True)
+
+
+def oracle_threads():
+    import oracle
+    return oracle.default_threads()
+
+
+def _profile_record(kernel, workload, kind):
+    """A committed rocprofv3 counter record of `kernel` on `workload`, or None
+    when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"{kernel.replace('_kernel', '')}_{workload}_{kind}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -287,7 +416,27 @@ def measured_traffic(kernel, workload):
 
     if rec.get("kernel_sha") != kernel_sha(kernel):
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from committed FETCH_SIZE / WRITE_SIZE
+    counter runs, or None (absent, or taken on other sources)."""
+    rec = _profile_record(kernel, workload, "traffic")
+    return None if rec is None else rec.get("bytes_per_launch")
+
+
+def counter_fields(kernel, workload, kernel_ms):
+    """Counter-based figures for the roofline record: achieved HBM GB/s (the
+    traffic counters' bytes per launch over the kernel's time in this run)
+    and the matrix cores' busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over
+    active cycles x SIMDs); None where no current record exists."""
+    traffic = measured_traffic(kernel, workload)
+    sq = _profile_record(kernel, workload, "sq")
+    return {
+        "achieved_gbps": None if traffic is None else traffic / (kernel_ms * 1e-3) / 1e9,
+        "mfma_busy": None if sq is None else sq.get("mfma_busy"),
+    }
 
 
 def cpu_baseline(inp, wl, budget_s, fused=False):
@@ -358,6 +507,8 @@ def main():
                     help="fused time-mix inputs (WKV7_FUSED_INPUTS)")
     ap.add_argument("--epilogue", action="store_true",
                     help="time the epilogue (group norm, bonus, gate) instead of the scan")
+    ap.add_argument("--algo", default="auto", choices=("auto", "scan", "chunked"),
+                    help="backward form (wkv7_algo): scan times the step-by-step reverse scan")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run a plain device copy of this many bytes (the "
                          "reference point for the HBM traffic counters)")
@@ -374,6 +525,9 @@ def main():
     from linear_attention_rnn_wkv7_amd import api
     from linear_attention_rnn_wkv7_amd.synthetic import WORKLOADS, make_inputs
 
+    from linear_attention_rnn_wkv7_amd.synthetic import RWKV8_WORKLOADS
+    if args.workload in RWKV8_WORKLOADS:
+        return rwkv8_bench(args, RWKV8_WORKLOADS[args.workload])
     wl = WORKLOADS[args.workload]
     if args.epilogue:
         return epilogue_bench(args, wl)
@@ -404,7 +558,8 @@ def main():
         if ev:
             ev[1].record(stream)
         api.wkv7_backward(*(inp[n] for n in names), inp["dy"], inp["s0"], inp["dsT"], ck,
-                          chunk=C, workspace=ws, out=grads, stream=stream, fused=fused)
+                          chunk=C, workspace=ws, out=grads, stream=stream, fused=fused,
+                          algo=args.algo)
         if ev:
             ev[2].record(stream)
 
@@ -438,7 +593,7 @@ def main():
             raise RuntimeError(f"non-finite values in {n}")
 
     fwd_flops, bwd_flops, fwd_bytes, bwd_bytes = algorithmic(wl)
-    chunked = N == 64 and C == 64   # the reverse scan's chunk form applies
+    chunked = N == 64 and C == 64 and args.algo != "scan"   # the chunk form runs
     achieved = bwd_flops / (bwd_ms * 1e-3)
     kernel = "wkv7_bwdc_kernel" if chunked else "wkv7_bwd_kernel"
     traffic = measured_traffic(kernel, wl.name)
@@ -459,7 +614,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "N": N, "chunk": C,
                    "input_dtype": wl.dtype, "s0": wl.has_s0, "dsT": wl.has_dsT,
-                   **({"fused_inputs": True} if fused else {})},
+                   **({"fused_inputs": True} if fused else {}),
+                   **({"backward": args.algo} if args.algo != "auto" else {})},
         "roofline": {
             "kernel": kernel,
             "bound": "mfma" if chunked else "alu",
@@ -468,6 +624,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP32_VALU,
             "traffic": traffic,
+            "mfma_type": "v_mfma_f32_16x16x4f32" if chunked else None,
+            **counter_fields(kernel, wl.name, bwd_ms),
         },
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,

@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 _CSRC = "linear_attention_rnn_wkv7_amd/csrc/"
 KERNEL_SOURCES = tuple(_CSRC + f for f in ("wkv7_bwd.hip", "wkv7_bwdc.hip", "wkv7_fwd.hip",
                                            "wkv7_fwdc.hip", "wkv7_decode.hip", "wkv7_split.hip",
-                                           "wkv7_epilogue.hip", "wkv7_device.h"))
+                                           "wkv7_epilogue.hip", "wkv7_device.h", "rwkv8.hip"))
 # the sources each kernel is built from (its traffic record is stale once
 # one of them changes)
 _KERNEL_FILES = {
@@ -34,6 +34,8 @@ _KERNEL_FILES = {
     "wkv7_decode_kernel": ("wkv7_decode.hip", "wkv7_device.h"),
     "epi_fwd_kernel": ("wkv7_epilogue.hip", "wkv7_device.h"),
     "epi_bwd_kernel": ("wkv7_epilogue.hip", "wkv7_device.h"),
+    "rwkv8_fwd_kernel": ("rwkv8.hip",),
+    "rwkv8_bwd_kernel": ("rwkv8.hip",),
 }
 
 
@@ -48,7 +50,8 @@ def kernel_sha(kernel=None):
 
 
 def _short(name):
-    m = re.search(r"(wkv7_\w+_kernel|epi_\w+_kernel|compose_\w+_kernel|flag_reduce_kernel|fill_kernel)", name)
+    m = re.search(r"(wkv7_\w+_kernel|rwkv8_\w+_kernel|epi_\w+_kernel|compose_\w+_kernel|sum_\w+_kernel|"
+                  r"flag_reduce_kernel|fill_kernel)", name)
     if m:
         return m.group(1)
     return name[:60]
@@ -57,26 +60,29 @@ def _short(name):
 def stats(csv_path, cmd, out):
     rows = list(csv.DictReader(open(csv_path)))
     lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "```", cmd, "```", "",
-             "| kernel | calls | total ms | average us | min us | max us | % |",
-             "|---|---|---|---|---|---|---|"]
+             "| kernel | calls | total ms | average us | min us | max us | % | sources sha |",
+             "|---|---|---|---|---|---|---|---|"]
     for r in rows:
         name = r["Name"]
-        if "wkv7" not in name and float(r.get("Percentage", 0)) < 1.0:
+        if "wkv7" not in name and "rwkv8" not in name and float(r.get("Percentage", 0)) < 1.0:
             continue
-        lines.append(f"| `{_short(name)}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+        k = _short(name)
+        sha = kernel_sha(k) if k in _KERNEL_FILES else "-"
+        lines.append(f"| `{k}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
                      f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
-                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} | `{sha}` |")
     lines.append("")
-    lines.append(f"Kernel sources sha: `{kernel_sha()}`")
+    lines.append("The sha of a kernel is that of the sources it is built from; a row is current "
+                 "while it matches.")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     return out
 
 
-def sq(csv_path, cmd, out, n_simd=1024, n_cu=256, n_xcd=8):
+def sq(csv_path, cmd, out, n_simd=1024, n_cu=256, n_xcd=8, workload=None):
     sums, disp = {}, {}
     for r in csv.DictReader(open(csv_path)):
-        m = re.search(r"(wkv7_\w+_kernel)", r["Kernel_Name"])
+        m = re.search(r"((?:wkv7|rwkv8)_\w+_kernel)", r["Kernel_Name"])
         if not m:
             continue
         k = m.group(1)
@@ -89,6 +95,7 @@ def sq(csv_path, cmd, out, n_simd=1024, n_cu=256, n_xcd=8):
         lines.append(f"| `{k}` | {c} | {v / len(disp[k]):.4e} |")
     lines += ["", "| kernel | MFMA busy / (active cycles x SIMDs) | LDS bank-conflict cycles per CU / active cycles |",
               "|---|---|---|"]
+    recs = {}
     for k in sorted(disp):
         n = len(disp[k])
         act = sums.get((k, "GRBM_GUI_ACTIVE"), 0.0) / n / n_xcd
@@ -96,9 +103,19 @@ def sq(csv_path, cmd, out, n_simd=1024, n_cu=256, n_xcd=8):
         bc = sums.get((k, "SQ_LDS_BANK_CONFLICT"), 0.0) / n
         if act > 0:
             lines.append(f"| `{k}` | {mf / (act * n_simd):.3f} | {bc / n_cu / act:.3f} |")
-    lines += ["", f"Kernel sources sha: `{kernel_sha()}`"]
+            recs[k] = {"mfma_busy": mf / (act * n_simd), "lds_conflict_frac": bc / n_cu / act,
+                       "kernel_sha": kernel_sha(k) if k in _KERNEL_FILES else None}
+    lines += ["", "Sources sha per kernel: " + ", ".join(
+        f"`{k}` `{r['kernel_sha']}`" for k, r in recs.items())]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
+    # one machine-readable record per kernel, read by bench.py
+    if workload:
+        for k, r in recs.items():
+            path = os.path.join(os.path.dirname(os.path.abspath(out)),
+                                f"{k.replace('_kernel', '')}_{workload}_sq.json")
+            with open(path, "w") as fh:
+                json.dump(dict(r, workload=workload, kernel=k, command=cmd), fh, indent=1)
     return out
 
 
@@ -159,6 +176,7 @@ if __name__ == "__main__":
     q.add_argument("--csv", required=True)
     q.add_argument("--cmd", required=True)
     q.add_argument("--out", required=True)
+    q.add_argument("--workload")
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
@@ -171,7 +189,7 @@ if __name__ == "__main__":
     if args.what == "stats":
         print(stats(args.csv, args.cmd, args.out))
     elif args.what == "sq":
-        print(sq(args.csv, args.cmd, args.out))
+        print(sq(args.csv, args.cmd, args.out, workload=args.workload))
     else:
         print(json.dumps(traffic(args.fetch, args.write, args.kernel, args.copy_bytes,
                                  args.workload, args.cmd, args.out)))
