@@ -62,6 +62,14 @@ __device__ __forceinline__ int xs(int r, int col)
     return (r << 6) + ((((col >> 2) ^ f) & 15) << 2) + (col & 3);
 }
 
+// 16 x 16 fp32 LDS matrices, the 16-byte groups of row t XOR-swizzled by
+// (t >> 2) & 3: reads of elements 4 g .. 4 g + 3 of rows 0..15 meet distinct
+// banks.
+__device__ __forceinline__ int gm(int t, int u)
+{
+    return (t << 4) + ((((u >> 2) ^ (t >> 2)) & 3) << 2) + (u & 3);
+}
+
 __device__ __forceinline__ float4 lds4(const float *s, int o)
 {
     return *reinterpret_cast<const float4 *>(s + o);
@@ -172,11 +180,11 @@ __device__ __forceinline__ bool decay_ok(float d)
     return d >= kDecayMin && d <= 1.f;   // false for NaN
 }
 
-__device__ void poison(float *p, int64_t n, int tid)
+__device__ void poison(float *p, int64_t n, int tid, int nthreads = kThreads)
 {
     if (!p) return;
     const float nan = __builtin_nanf("");
-    for (int64_t i = tid; i < n; i += kThreads) p[i] = nan;
+    for (int64_t i = tid; i < n; i += nthreads) p[i] = nan;
 }
 
 struct FwdArgs {
@@ -187,138 +195,273 @@ struct FwdArgs {
     unsigned *fault;
 };
 
-// One workgroup per (b, h); wave w holds columns 16 w .. 16 w + 15 of R as
-// four 16 x 16 accumulator tiles (rows 16 lb + 4 (lane / 16) + i, column
-// 16 w + lane % 16), so the tiles of a chunk need no exchange between waves.
-__global__ void __launch_bounds__(kThreads) rwkv8_fwd_kernel(FwdArgs p)
+constexpr int kFwdThreads = 512;   // 4 consumer + 4 producer waves
+
+// One workgroup of eight waves per (b, h).  Waves 0-3 ("consumers") hold R
+// as accumulator tiles (wave w: columns 16 w .. 16 w + 15; element i of tile
+// lb: row 16 lb + 4 (lane / 16) + i, column 16 w + lane % 16), so the tiles
+// of a chunk need no exchange between waves, and run the four tiles of
+// chunk cc.  Waves 4-7 ("producers") meanwhile prepare chunk cc + 1,
+// producer pw its tile pw (sigma, the rho_norm chain, chat, qhat and the
+// tile's Gram), from the chunk's raw queries, which they staged during the
+// chunk before (so that every producer sees all of them and runs the
+// rho_norm chain itself, without waiting for the others), and stage chunk
+// cc + 2.  All of a chunk's operands are in LDS, double-buffered by chunk
+// parity; one barrier per chunk.  The products over the steps of a tile take
+// step t0 + 4 g + kk in the K slot of row group g at step kk, so that qhat
+// and v, kept transposed ([latent or embedding][step]), and the tile's Gram
+// are read 16 bytes at a time.
+__global__ void __launch_bounds__(kFwdThreads) rwkv8_fwd_kernel(FwdArgs p)
 {
-    __shared__ __align__(16) float Qs[kN * kN];   // q, then qhat
-    __shared__ __align__(16) float Vs[kN * kN];
-    __shared__ __align__(16) float Cs[kN * kN];   // chat
-    __shared__ float Ms[4][kS * kMs];
-    __shared__ float sig[kN], dlt[4 * kN], nch[kN], nend[kN];
+    __shared__ __align__(16) float Qr[2][kN * kN];   // raw q [t][l]
+    __shared__ __align__(16) float Qt[2][kN * kN];   // qhat [l][t]
+    __shared__ __align__(16) float Cs[2][kN * kN];   // chat [t][l]
+    __shared__ __align__(16) float Vt[2][kN * kN];   // v [e][t]
+    __shared__ __align__(16) float Qp[4][kS * kN];   // qhat of producer pw's tile [u][l]
+    __shared__ __align__(16) float Ms[2][4][kS * kS];   // the tiles' Grams, gm layout
+    __shared__ float sig[4][kS];                     // sigma of producer pw's tile
     __shared__ int bad;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, c = lane & 15;
     const int64_t bh = blockIdx.x, H = p.H, T = p.T;
     const int64_t b = bh / H, h = bh % H;
+    const int nck = p.nck;
     const float *qg = p.q + bh * T * kN;
     const float *vg = p.v + (b * p.Hv + (p.Hv == 1 ? 0 : h)) * T * kN;
     float *yg = p.y ? p.y + bh * T * kN : nullptr;
     const float *dec = p.decay + h * kN;
+    auto steps = [&](int cc) {
+        const int64_t rem = T - (int64_t)cc * kCk;
+        return (int)(rem < kCk ? rem : kCk);
+    };
 
-    const float dl = dec[lane];   // prep: lane = latent
     if (tid == 0) bad = 0;
     __syncthreads();
-    if (w == 0 && !decay_ok(dl)) bad = 1;
+    if (w == 0 && !decay_ok(dec[lane])) bad = 1;
     __syncthreads();
     if (bad) {
-        poison(yg, T * kN, tid);
-        poison(p.rhoT ? p.rhoT + bh * kN * kN : nullptr, kN * kN, tid);
-        poison(p.normT ? p.normT + bh * kN : nullptr, kN, tid);
-        poison(p.ckpt ? p.ckpt + bh * p.nck * kRec : nullptr, (int64_t)p.nck * kRec, tid);
+        poison(yg, T * kN, tid, kFwdThreads);
+        poison(p.rhoT ? p.rhoT + bh * kN * kN : nullptr, kN * kN, tid, kFwdThreads);
+        poison(p.normT ? p.normT + bh * kN : nullptr, kN, tid, kFwdThreads);
+        poison(p.ckpt ? p.ckpt + bh * nck * kRec : nullptr, (int64_t)nck * kRec, tid, kFwdThreads);
         if (tid == 0) __hip_atomic_fetch_or(p.fault, (unsigned)WKV7_FAULT_RWKV8_DECAY, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    const float inv_dl = 1.f / dl;
-    float p16l = dl * dl;
-    p16l *= p16l;
-    p16l *= p16l;
-    p16l *= p16l;
 
-    // the decays of this lane's state rows and their 16th powers
-    float dr[4][4], p16r[4][4];
-    f4 Racc[4];
-#pragma unroll
-    for (int lb = 0; lb < 4; ++lb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int l = 16 * lb + 4 * g + i;
-            const float x = dec[l];
-            float x16 = x * x;
-            x16 *= x16;
-            x16 *= x16;
-            x16 *= x16;
-            dr[lb][i] = x;
-            p16r[lb][i] = x16;
-            Racc[lb][i] = p.rho0 ? p.rho0[bh * kN * kN + l * kN + 16 * w + c] : 0.f;
-        }
-    if (w == 0) nch[lane] = p.norm0 ? p.norm0[bh * kN + lane] : 0.f;
-
-    for (int cc = 0; cc < p.nck; ++cc) {
-        const int64_t tc = (int64_t)cc * kCk;
-        const int nst = (int)(T - tc < kCk ? T - tc : kCk);
-        __syncthreads();   // the previous chunk is done with every LDS array
-        stage(Qs, qg, tc, nst, tid);
-        stage(Vs, vg, tc, nst, tid);
-        if (w == 0 && cc > 0) nch[lane] = nend[lane];
-        if (p.ckpt) {   // the state before this chunk
-            float *ck = p.ckpt + (bh * p.nck + cc) * kRec;
-#pragma unroll
-            for (int lb = 0; lb < 4; ++lb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ck[(16 * lb + 4 * g + i) * kN + 16 * w + c] = Racc[lb][i];
-            if (w == 0) ck[kN * kN + lane] = nch[lane];
-        }
-        __syncthreads();
-        prep_chunk(Qs, Cs, sig, dlt, nch, nullptr, nend, dl, inv_dl, p16l, nst, tid);
-        __syncthreads();
-        if (yg) gram_tile(Cs, Qs, Ms[w], kS * w, lane);
-        __syncthreads();
-        for (int k = 0; k < 4; ++k) {
-            const int t0 = kS * k;
-            if (t0 >= nst) break;
-            const int ns = nst - t0 < kS ? nst - t0 : kS;
-            if (yg) {
-                // Y = Chat R0 + M V for columns 16 w ..: rows t0 + 4 g + i
-                f4 Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int lb = 0; lb < 4; ++lb) {
-                    const float4 a = lds4(Cs, xs(t0 + c, 16 * lb + 4 * g));
-                    Y = mfma(a.x, Racc[lb][0], Y);
-                    Y = mfma(a.y, Racc[lb][1], Y);
-                    Y = mfma(a.z, Racc[lb][2], Y);
-                    Y = mfma(a.w, Racc[lb][3], Y);
-                }
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    Y = mfma(Ms[k][c * kMs + 4 * kk + g], Vs[xs(t0 + 4 * kk + g, 16 * w + c)], Y);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = t0 + 4 * g + i;
-                    if (t < nst) yg[(tc + t) * kN + 16 * w + c] = Y[i];
-                }
-            }
-            // R <- diag(p_ns) (R + Qhat^T V)
-#pragma unroll
-            for (int lb = 0; lb < 4; ++lb)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    Racc[lb] = mfma(Qs[xs(t0 + 4 * kk + g, 16 * lb + c)], Vs[xs(t0 + 4 * kk + g, 16 * w + c)],
-                                    Racc[lb]);
-            if (ns == kS) {
-#pragma unroll
-                for (int lb = 0; lb < 4; ++lb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) Racc[lb][i] *= p16r[lb][i];
-            } else {
-#pragma unroll
-                for (int lb = 0; lb < 4; ++lb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) Racc[lb][i] *= powi(dr[lb][i], ns);
-            }
-        }
-    }
-    if (p.rhoT) {
+    if (w < 4) {
+        // ================= consumers =================
+        // the decays of this lane's state rows and their 16th powers
+        float dr[4][4], p16r[4][4];
+        f4 Racc[4];
 #pragma unroll
         for (int lb = 0; lb < 4; ++lb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                p.rhoT[bh * kN * kN + (16 * lb + 4 * g + i) * kN + 16 * w + c] = Racc[lb][i];
+            for (int i = 0; i < 4; ++i) {
+                const int l = 16 * lb + 4 * g + i;
+                const float x = dec[l];
+                float x16 = x * x;
+                x16 *= x16;
+                x16 *= x16;
+                x16 *= x16;
+                dr[lb][i] = x;
+                p16r[lb][i] = x16;
+                Racc[lb][i] = p.rho0 ? p.rho0[bh * kN * kN + l * kN + 16 * w + c] : 0.f;
+            }
+        __syncthreads();   // chunk 0 staged (and chunk 1's queries)
+        __syncthreads();   // chunk 0 prepared
+        for (int cc = 0; cc < nck; ++cc) {
+            const int bb = cc & 1;
+            const int64_t tc = (int64_t)cc * kCk;
+            const int nst = steps(cc);
+            const float *C = Cs[bb], *Q = Qt[bb], *V = Vt[bb];
+            if (p.ckpt) {   // the state before this chunk (rho part)
+                float *ck = p.ckpt + (bh * nck + cc) * kRec;
+#pragma unroll
+                for (int lb = 0; lb < 4; ++lb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ck[(16 * lb + 4 * g + i) * kN + 16 * w + c] = Racc[lb][i];
+            }
+            for (int k = 0; k < 4; ++k) {
+                const int t0 = kS * k;
+                if (t0 >= nst) break;
+                const int ns = nst - t0 < kS ? nst - t0 : kS;
+                // v of steps t0 + 4 g .. + 3, column 16 w + c
+                const float4 v4 = lds4(V, xs(16 * w + c, t0 + 4 * g));
+                if (yg) {
+                    // Y = Chat R0 + M V for columns 16 w ..: rows t0 + 4 g + i
+                    const float4 m4 = lds4(Ms[bb][k], gm(c, 4 * g));
+                    f4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int lb = 0; lb < 4; ++lb) {
+                        const float4 a = lds4(C, xs(t0 + c, 16 * lb + 4 * g));
+                        Y = mfma(a.x, Racc[lb][0], Y);
+                        Y = mfma(a.y, Racc[lb][1], Y);
+                        Y = mfma(a.z, Racc[lb][2], Y);
+                        Y = mfma(a.w, Racc[lb][3], Y);
+                    }
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) Y = mfma(el(m4, kk), el(v4, kk), Y);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = t0 + 4 * g + i;
+                        if (t < nst) yg[(tc + t) * kN + 16 * w + c] = Y[i];
+                    }
+                }
+                // R <- diag(p_ns) (R + Qhat^T V)
+#pragma unroll
+                for (int lb = 0; lb < 4; ++lb) {
+                    const float4 q4 = lds4(Q, xs(16 * lb + c, t0 + 4 * g));
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) Racc[lb] = mfma(el(q4, kk), el(v4, kk), Racc[lb]);
+                }
+                if (ns == kS) {
+#pragma unroll
+                    for (int lb = 0; lb < 4; ++lb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) Racc[lb][i] *= p16r[lb][i];
+                } else {
+#pragma unroll
+                    for (int lb = 0; lb < 4; ++lb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) Racc[lb][i] *= powi(dr[lb][i], ns);
+                }
+            }
+            __syncthreads();   // chunk cc consumed, chunk cc + 1 prepared
+        }
+        if (p.rhoT) {
+#pragma unroll
+            for (int lb = 0; lb < 4; ++lb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    p.rhoT[bh * kN * kN + (16 * lb + 4 * g + i) * kN + 16 * w + c] = Racc[lb][i];
+        }
+        return;
     }
-    __syncthreads();
-    if (p.normT && w == 0) p.normT[bh * kN + lane] = nend[lane];
+
+    // ================= producers =================
+    const int pw = w - 4, t0 = kS * pw;
+    const float dl = dec[lane];   // lane = latent
+    const float inv_dl = 1.f / dl;
+    float n_carry = p.norm0 ? p.norm0[bh * kN + lane] : 0.f;   // n at the start of the next chunk to prepare
+    // rows 16 pw + 4 k + lane / 16, columns 4 (lane % 16) .. + 3 of a chunk
+    const int srow = t0 + (lane >> 4), scol = 4 * (lane & 15);
+    float4 qx[4], vx[4], vnext[4];
+    auto issue = [&](int cc, float4 (&qo)[4], float4 (&vo)[4]) {
+        const int64_t tc = (int64_t)cc * kCk;
+        const int nst = steps(cc);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int row = srow + 4 * k;
+            qo[k] = vo[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (row < nst) {
+                qo[k] = *reinterpret_cast<const float4 *>(qg + (tc + row) * kN + scol);
+                vo[k] = *reinterpret_cast<const float4 *>(vg + (tc + row) * kN + scol);
+            }
+        }
+    };
+    auto put = [&](float *dst, const float4 (&x)[4]) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) st4(dst, xs(srow + 4 * k, scol), x[k]);
+    };
+    auto put_t = [&](float *dst, const float4 (&x)[4]) {   // transposed: [column][step]
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[xs(scol + i, srow + 4 * k)] = el(x[k], i);
+    };
+    // chunk X from its raw queries in Qr[X & 1]: this producer's tile
+    auto prep = [&](int X) {
+        const int xb = X & 1;
+        const int nst = steps(X);
+        const float *Q = Qr[xb];
+        {   // sigma of the tile's steps: lane (step t0 + lane / 4, quarter lane % 4)
+            const int t = t0 + (lane >> 2), part = lane & 3;
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float4 x = lds4(Q, xs(t, 16 * part + 4 * j));
+                s += (x.x + x.y) + (x.z + x.w);
+            }
+            s += __shfl_xor(s, 1);
+            s += __shfl_xor(s, 2);
+            if (part == 0) sig[pw][lane >> 2] = s + kEps;
+        }
+        if (pw == 0 && p.ckpt) p.ckpt[(bh * nck + X) * kRec + kN * kN + lane] = n_carry;
+        // the rho_norm chain over the chunk (the queries of each other tile
+        // read together, then its steps); c, chat, qhat on this tile
+        auto chain16 = [&](int tt, float &n) {
+            float qv[kS];
+#pragma unroll
+            for (int u = 0; u < kS; ++u) qv[u] = Q[xs(kS * tt + u, lane)];
+#pragma unroll
+            for (int u = 0; u < kS; ++u)
+                if (kS * tt + u < nst) n = fmaf(dl, n, qv[u]);
+        };
+        float n = n_carry;
+        for (int tt = 0; tt < pw; ++tt) chain16(tt, n);
+        float pu = 1.f, ip = 1.f, qh[kS];
+#pragma unroll
+        for (int u = 0; u < kS; ++u) {
+            const int t = t0 + u, o = xs(t, lane);
+            const float q = Q[o];
+            const float cv = q * __builtin_amdgcn_rcpf(sig[pw][u] * (n + kEps));
+            ip *= inv_dl;
+            Cs[xb][o] = cv * pu;
+            qh[u] = q * ip;
+            Qp[pw][xs(u, lane)] = qh[u];
+            if (t < nst) n = fmaf(dl, n, q);
+            pu *= dl;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            st4(Qt[xb], xs(lane, t0 + 4 * j), make_float4(qh[4 * j], qh[4 * j + 1], qh[4 * j + 2], qh[4 * j + 3]));
+        for (int tt = pw + 1; tt < kCk / kS; ++tt) chain16(tt, n);
+        n_carry = n;
+        if (yg) {   // M[t][u] = chat_t . qhat_u (u < t) over the tile: lane (g, c) holds M[4 g + i][c]
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const float4 a = lds4(Cs[xb], xs(t0 + c, 16 * s4 + 4 * g));
+                const float4 b = lds4(Qp[pw], xs(c, 16 * s4 + 4 * g));
+                acc = mfma(a.x, b.x, acc);
+                acc = mfma(a.y, b.y, acc);
+                acc = mfma(a.z, b.z, acc);
+                acc = mfma(a.w, b.w, acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ms[xb][pw][gm(4 * g + i, c)] = c < 4 * g + i ? acc[i] : 0.f;
+        }
+    };
+
+    // chunk 0 and the queries of chunk 1; v of chunk 1 waits in registers
+    issue(0, qx, vx);
+    put(Qr[0], qx);
+    put_t(Vt[0], vx);
+    if (nck > 1) {
+        issue(1, qx, vnext);
+        put(Qr[1], qx);
+    }
+    __syncthreads();   // chunk 0 staged (and chunk 1's queries)
+    prep(0);
+    __syncthreads();   // chunk 0 prepared
+    for (int cc = 0; cc < nck; ++cc) {
+        // during chunk cc: chunk cc + 1's values into their buffer (free since
+        // chunk cc - 1), chunk cc + 1 prepared, chunk cc + 2 staged
+        const bool has2 = cc + 2 < nck;
+        if (has2) issue(cc + 2, qx, vx);
+        if (cc + 1 < nck) {
+            put_t(Vt[(cc + 1) & 1], vnext);
+            prep(cc + 1);
+        }
+        if (has2) {
+            put(Qr[cc & 1], qx);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) vnext[k] = vx[k];
+        }
+        __syncthreads();   // chunk cc consumed, chunk cc + 1 prepared
+    }
+    if (p.normT && pw == 0) p.normT[bh * kN + lane] = n_carry;
 }
 
 struct BwdArgs {
@@ -754,7 +897,7 @@ hipError_t launch_fwd(const Dims &d, const float *q, const float *v, const float
     a.nck = (int)d.nck;
     a.fault = wkv7::fault_word();
     if (!a.fault) return hipErrorInvalidDevicePointer;
-    hipLaunchKernelGGL(rwkv8_fwd_kernel, dim3((unsigned)(d.B * d.H)), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(rwkv8_fwd_kernel, dim3((unsigned)(d.B * d.H)), dim3(kFwdThreads), 0, stream, a);
     return hipGetLastError();
 }
 

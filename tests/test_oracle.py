@@ -1,4 +1,6 @@
 """The fp64 oracle against facts that do not come from the oracle itself."""
+import zlib
+
 import numpy as np
 import pytest
 
@@ -8,7 +10,7 @@ import oracle_pins as P
 @pytest.mark.parametrize("name", list(P.ALL_PINS))
 def test_oracle_pin(name):
     fn, tol = P.ALL_PINS[name]
-    err = fn(np.random.default_rng(hash(name) % 2**32), None)
+    err = fn(np.random.default_rng(zlib.crc32(name.encode())), None)
     assert err <= tol, f"{name}: rel err {err:.3e} > {tol:.0e}"
 
 
