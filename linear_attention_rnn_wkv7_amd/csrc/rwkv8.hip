@@ -146,7 +146,7 @@ __device__ __forceinline__ void prep_chunk(float *Qs, float *Cs, float *sig, flo
         const int t = kS * w + u;
         const int o = xs(t, lane);
         const float q = Qs[o];
-        const float cv = q / (sig[t] * (n + kEps));
+        const float cv = q * __builtin_amdgcn_rcpf(sig[t] * (n + kEps));
         ip *= inv_dl;
         Cs[o] = cv * pw;
         Qs[o] = q * ip;
@@ -700,20 +700,30 @@ __global__ void __launch_bounds__(kThreads) rwkv8_bwd_kernel(BwdArgs p)
         {
             float pr[kS];
             float n = nts[w * kN + lane], pwr = 1.f, lm = 0.f, pl = 1.f;
+            // the tile's operands, read ahead of the chain through n
+            float qv[kS], dcv[kS], rsv[kS];
+#pragma unroll
+            for (int u = 0; u < kS; ++u) {
+                const int t = t0 + u, o = xs(t, lane);
+                qv[u] = Qs[o];
+                dcv[u] = DCs[o];
+                rsv[u] = __builtin_amdgcn_rcpf(sig[t]);
+            }
 #pragma unroll
             for (int u = 0; u < kS; ++u) {
                 pr[u] = 0.f;
                 if (u < ns) {
                     const int t = t0 + u, o = xs(t, lane);
                     pwr *= dl;
-                    const float q = Qs[o] * pwr;
-                    const float s = sig[t], ne = n + kEps;
-                    const float gw = DCs[o] / ne;
-                    const float x = -gw * (q / (s * ne));
+                    const float q = qv[u] * pwr;
+                    const float rne = __builtin_amdgcn_rcpf(n + kEps);
+                    const float gw = dcv[u] * rne;
+                    const float qs = q * rsv[u];
+                    const float x = -gw * (qs * rne);
                     Cs[o] = n;
                     Vs[o] = gw;
                     Ys[o] = x;
-                    pr[u] = gw * (q / s);
+                    pr[u] = gw * qs;
                     lm = fmaf(pl, x, lm);   // sum_u d^u x_u
                     pl *= dl;
                     n = fmaf(dl, n, q);
@@ -764,7 +774,7 @@ __global__ void __launch_bounds__(kThreads) rwkv8_bwd_kernel(BwdArgs p)
             }
             for (int u = ns - 1; u >= 0; --u) {
                 const int t = t0 + u, o = xs(t, lane);
-                const float dqv = DQs[o] + (Vs[o] - ssum[w][u]) / sig[t] + Gn;
+                const float dqv = DQs[o] + (Vs[o] - ssum[w][u]) * __builtin_amdgcn_rcpf(sig[t]) + Gn;
                 dqg[(tc + t) * kN + lane] = dqv;
                 ddn = fmaf(Gn, Cs[o], ddn);
                 Gn = fmaf(dl, Gn, Ys[o]);
