@@ -73,3 +73,15 @@ def test_failed_launch_status():
     y, sT, ck = _forward(inp)   # the next call is not affected
     torch.cuda.synchronize()
     assert torch.isfinite(y).all()
+    # the backward reports its failed launch the same way
+    assert L.wkv7_test_hook(_lib.WKV7_HOOK_FAIL_LAUNCHES, 1) == _lib.WKV7_OK
+    try:
+        with pytest.raises(_lib.Wkv7Error) as e:
+            api.wkv7_backward(*(inp[n] for n in H.IN), inp["dy"], inp["s0"], inp["dsT"], ck)
+        assert e.value.status == _lib.WKV7_ERR_HIP
+    finally:
+        L.wkv7_test_hook(_lib.WKV7_HOOK_FAIL_LAUNCHES, 0)
+    torch.cuda.synchronize()
+    g = api.wkv7_backward(*(inp[n] for n in H.IN), inp["dy"], inp["s0"], inp["dsT"], ck)
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(x).all() for x in g.values() if x is not None)
